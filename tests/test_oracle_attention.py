@@ -1,0 +1,283 @@
+"""Pins of the oracle's cache layouts and fp64 sparse attention.  No GPU."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention, brute, cache, formats
+from quantized_kv_top_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _src_np(t):
+    return wl.to_numpy_src(t)
+
+
+def _oracle_cache(w, kind, k_scale=None, v_scale=None):
+    c = cache.OracleCache(kind, w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim,
+                          k_scale, v_scale)
+    c.write(_src_np(w.k_src), _src_np(w.v_src), w.src_dtype, w.slot_mapping)
+    return c
+
+
+# ---------------------------------------------------------------------------
+# layouts and capacity
+# ---------------------------------------------------------------------------
+
+def test_layout_sizes_match_pages():
+    g = json.load(open(os.path.join(GOLDEN, "int8_layout.json")))
+    D = g["inline_slot_head_dim"]
+    assert cache.row_bytes("int8_inline", D) == g["inline_slot_bytes"]
+    assert g["inline_slot_bytes"] % g["alignment_unit"] != 0
+    assert cache.row_bytes("int8", D) % g["alignment_unit"] == 0
+    cfg = g["bytes_per_token_config"]
+    for kind, want in g["bytes_per_token_per_gpu"].items():
+        assert cache.bytes_per_token(kind, cfg["num_kv_heads"], cfg["head_dim"]) == want
+    # identical memory cost of the two int8 layouts
+    assert (cache.bytes_per_token("int8", 2, 256)
+            == cache.bytes_per_token("int8_inline", 2, 256))
+
+
+def test_pool_capacity_ratios():
+    pool = wl.E2E_POOL_BYTES
+    t = {k: cache.pool_tokens(pool, k, 2, 256, 64) for k in ("bf16", "int8", "e4m3")}
+    assert t["e4m3"] / t["bf16"] == pytest.approx(2.0, abs=1e-4)
+    # int8 pays 4 scale bytes per 256 data bytes: ratio 2048/1040
+    assert t["int8"] / t["bf16"] == pytest.approx(2048 / 1040, abs=1e-4)
+    for k, v in t.items():
+        assert v % 64 == 0
+        assert v * cache.bytes_per_token(k, 2, 256) <= pool
+
+
+def test_inline_and_side_layouts_hold_identical_values():
+    w = wl.tiny()
+    side = _oracle_cache(w, "int8")
+    inl = _oracle_cache(w, "int8_inline")
+    slots = np.arange(side.num_slots)
+    for which in ("k", "v"):
+        np.testing.assert_array_equal(side.dequant(slots, which), inl.dequant(slots, which))
+        D = w.head_dim
+        np.testing.assert_array_equal(getattr(side, which)[..., :D],
+                                      getattr(inl, which)[..., :D])
+        tail = np.ascontiguousarray(getattr(inl, which)[..., D:]).view("<f4")[..., 0]
+        np.testing.assert_array_equal(tail, side.kv_scale[..., 0 if which == "k" else 1])
+
+
+def test_write_skips_negative_slots_and_matches_quantizer():
+    w = wl.tiny()
+    sm = w.slot_mapping.copy()
+    sm[::3] = -1
+    c = cache.OracleCache("int8", w.num_blocks, w.block_size, 1, w.head_dim)
+    c.write(_src_np(w.k_src), _src_np(w.v_src), "fp32", sm)
+    kept = sm >= 0
+    assert np.all(c.k[np.setdiff1d(np.arange(c.num_slots), sm[kept])] == 0)
+    q, s = formats.int8_quantize(_src_np(w.k_src)[kept])
+    np.testing.assert_array_equal(c.k[sm[kept]].view(np.int8), q)
+    np.testing.assert_array_equal(c.kv_scale[sm[kept], :, 0], s)
+
+
+# ---------------------------------------------------------------------------
+# attention closed forms and library special cases
+# ---------------------------------------------------------------------------
+
+def _single_seq(kind, ctx, Hq, Hkv, D, BS, k, v, seed=0):
+    rng = np.random.default_rng(seed)
+    nb = ctx // BS
+    bt = rng.permutation(nb).reshape(1, nb).astype(np.int32)
+    slots = wl.slot_mapping_for(bt, 0, np.arange(ctx), BS)
+    c = cache.OracleCache(kind, nb, BS, Hkv, D,
+                          *( (formats.e4m3_calibrate_scale(k), formats.e4m3_calibrate_scale(v))
+                             if kind == "e4m3" else (None, None)))
+    c.write(k, v, "fp32", slots)
+    return c, bt
+
+
+def test_uniform_softmax_on_equal_keys():
+    ctx, Hq, Hkv, D, BS = 64, 8, 2, 128, 16
+    rng = np.random.default_rng(1)
+    key = rng.standard_normal((1, Hkv, D)).astype(np.float32)
+    k = np.repeat(key, ctx, axis=0)
+    v = rng.standard_normal((ctx, Hkv, D)).astype(np.float32)
+    for kind in cache.KINDS:
+        c, bt = _single_seq(kind, ctx, Hq, Hkv, D, BS, k, v)
+        q = formats.f32_to_bf16_bits(rng.standard_normal((1, Hq, D)).astype(np.float32))
+        idx = np.sort(rng.permutation(ctx)[:20]).astype(np.int32)[None]
+        out, lse = attention.sparse_attention(c, q, "bf16", [0], bt, idx, 0.125)
+        slots = attention.resolve_slots(bt[0], idx[0], BS)
+        vh = c.dequant(slots, "v")
+        kh = c.dequant(slots[:1], "k")
+        qf = formats.bf16_bits_to_f32(q[0]).astype(np.float64)
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            np.testing.assert_allclose(out[0, h], vh[:, g, :].mean(axis=0), rtol=1e-12, atol=1e-12)
+            s = 0.125 * float(qf[h] @ kh[0, g])
+            assert lse[0, h] == pytest.approx(s + np.log(20), rel=1e-12, abs=1e-12)
+
+
+def test_topk_one_returns_the_value_row():
+    w = wl.tiny()
+    c = _oracle_cache(w, "int8")
+    idx = np.array([[37]], np.int32)
+    out, lse = attention.sparse_attention(c, _src_np(w.q)[:1], "bf16", [0], w.block_table, idx,
+                                          w.sm_scale)
+    slot = attention.resolve_slots(w.block_table[0], [37], w.block_size)
+    np.testing.assert_array_equal(out[0], np.repeat(c.dequant(slot, "v")[0], 4, axis=0))
+    qf = formats.bf16_bits_to_f32(_src_np(w.q)[0]).astype(np.float64)
+    s = w.sm_scale * (qf @ c.dequant(slot, "k")[0, 0])
+    np.testing.assert_allclose(lse[0], s, rtol=1e-13)
+
+
+@pytest.mark.parametrize("kind", cache.KINDS)
+def test_full_causal_prefix_equals_dense_sdpa(kind):
+    """topk = the whole causal prefix reduces to dense causal attention, computed
+    here by torch's scaled_dot_product_attention in fp64 on the CPU over the
+    oracle's dequantized cache."""
+    ctx, Hq, Hkv, D, BS = 48, 8, 2, 128, 16
+    rng = np.random.default_rng(5)
+    k = rng.standard_normal((ctx, Hkv, D)).astype(np.float32)
+    v = rng.standard_normal((ctx, Hkv, D)).astype(np.float32)
+    c, bt = _single_seq(kind, ctx, Hq, Hkv, D, BS, k, v, seed=2)
+    rows = np.arange(ctx - 6, ctx)
+    q = formats.f32_to_bf16_bits(rng.standard_normal((len(rows), Hq, D)).astype(np.float32))
+    idx = np.full((len(rows), ctx), -1, np.int32)
+    for i, p in enumerate(rows):
+        idx[i, :p + 1] = rng.permutation(p + 1)       # order is irrelevant
+    sm = 0.0883883
+    out, lse = attention.sparse_attention(c, q, "bf16", np.zeros(len(rows), np.int32), bt, idx, sm)
+    slots = attention.resolve_slots(bt[0], np.arange(ctx), BS)
+    K = torch.from_numpy(c.dequant(slots, "k")).permute(1, 0, 2)     # [Hkv][ctx][D]
+    V = torch.from_numpy(c.dequant(slots, "v")).permute(1, 0, 2)
+    G = Hq // Hkv
+    K = K.repeat_interleave(G, dim=0)[None]
+    V = V.repeat_interleave(G, dim=0)[None]
+    Q = torch.from_numpy(formats.bf16_bits_to_f32(q).astype(np.float64)).permute(1, 0, 2)[None]
+    mask = torch.from_numpy(np.arange(ctx)[None, :] <= rows[:, None])
+    ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=mask, scale=sm)
+    np.testing.assert_allclose(out, ref[0].permute(1, 0, 2).numpy(), rtol=1e-10, atol=1e-12)
+    # lse against the explicit log-sum-exp of the dense logits
+    logits = torch.einsum("bhrd,bhcd->bhrc", Q, K) * sm
+    logits = logits.masked_fill(~mask, float("-inf"))
+    ref_lse = torch.logsumexp(logits, dim=-1)[0].permute(1, 0).numpy()
+    np.testing.assert_allclose(lse, ref_lse, rtol=1e-12)
+
+
+def test_brute_force_on_tiny():
+    w = wl.tiny()
+    c = _oracle_cache(w, "int8")
+    q = _src_np(w.q)
+    out, lse = attention.sparse_attention(c, q, "bf16", w.row_seq, w.block_table, w.topk_idx,
+                                          w.sm_scale)
+    for r in range(w.num_rows):
+        # brute: resolve slots by hand and dequantize from the stored bytes
+        slots = []
+        for j in w.topk_idx[r]:
+            blk = int(w.block_table[0][j // w.block_size])
+            slots.append(blk * w.block_size + int(j) % w.block_size)
+        kh = [[[float(x) * float(c.kv_scale[s, 0, 0]) for x in c.k[s, 0].view(np.int8)]]
+              for s in slots]
+        vh = [[[float(x) * float(c.kv_scale[s, 0, 1]) for x in c.v[s, 0].view(np.int8)]]
+              for s in slots]
+        qr = formats.bf16_bits_to_f32(q[r]).astype(np.float64).tolist()
+        bo, bl = brute.attend_row(qr, kh, vh, w.sm_scale)
+        np.testing.assert_allclose(out[r], np.array(bo), rtol=1e-11, atol=1e-13)
+        np.testing.assert_allclose(lse[r], np.array(bl), rtol=1e-12)
+
+
+def test_gqa_groups_are_contiguous():
+    """Head h reads KV head h // G: give each KV head a distinct constant value
+    row and read it back through a single selected token."""
+    ctx, Hq, Hkv, D, BS = 16, 8, 4, 128, 16
+    k = np.ones((ctx, Hkv, D), np.float32)
+    v = np.broadcast_to(np.arange(1, Hkv + 1, dtype=np.float32)[None, :, None], (ctx, Hkv, D)).copy()
+    c, bt = _single_seq("int8", ctx, Hq, Hkv, D, BS, k, v)
+    q = formats.f32_to_bf16_bits(np.ones((1, Hq, D), np.float32))
+    out, _ = attention.sparse_attention(c, q, "bf16", [0], bt, np.array([[3]], np.int32), 0.1)
+    vh = c.dequant(attention.resolve_slots(bt[0], [3], BS), "v")[0]
+    for h in range(Hq):
+        np.testing.assert_array_equal(out[0, h], vh[h // 2])
+        assert abs(out[0, h, 0] - (h // 2 + 1)) < 1e-6
+
+
+def test_order_and_padding_invariance_and_empty_rows():
+    w = wl.tiny()
+    c = _oracle_cache(w, "int8")
+    q = _src_np(w.q)
+    out, lse = attention.sparse_attention(c, q, "bf16", w.row_seq, w.block_table, w.topk_idx,
+                                          w.sm_scale)
+    rng = np.random.default_rng(3)
+    shuffled = np.stack([rng.permutation(r) for r in w.topk_idx])
+    padded = np.concatenate([shuffled, np.full((w.num_rows, 5), -1, np.int32)], axis=1)
+    padded = np.stack([rng.permutation(r) for r in padded])
+    o2, l2 = attention.sparse_attention(c, q, "bf16", w.row_seq, w.block_table, padded, w.sm_scale)
+    np.testing.assert_allclose(o2, out, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(l2, lse, rtol=1e-13)
+    empty = np.full((1, 7), -1, np.int32)
+    o3, l3 = attention.sparse_attention(c, q[:1], "bf16", [0], w.block_table, empty, w.sm_scale)
+    assert np.all(o3 == 0) and np.all(np.isneginf(l3))
+
+
+def test_e4m3_scale_folding_identity():
+    """k_scale = c equals k_scale = 1 with sm_scale * c; v_scale = c scales the
+    output by c (the two rearrangements the hoisting page makes)."""
+    ctx, Hq, Hkv, D, BS = 32, 4, 1, 128, 16
+    rng = np.random.default_rng(9)
+    k = rng.standard_normal((ctx, Hkv, D)).astype(np.float32)
+    v = rng.standard_normal((ctx, Hkv, D)).astype(np.float32)
+    nb = ctx // BS
+    bt = np.arange(nb).reshape(1, nb).astype(np.int32)
+    slots = np.arange(ctx)
+    q = formats.f32_to_bf16_bits(rng.standard_normal((1, Hq, D)).astype(np.float32))
+    idx = np.arange(ctx, dtype=np.int32)[None]
+    ca = cache.OracleCache("e4m3", nb, BS, Hkv, D, 0.25, 0.5)
+    ca.write(k, v, "fp32", slots)
+    cb = cache.OracleCache("e4m3", nb, BS, Hkv, D, 1.0, 1.0)
+    cb.k[:] = ca.k
+    cb.v[:] = ca.v
+    oa, la = attention.sparse_attention(ca, q, "bf16", [0], bt, idx, 0.1)
+    ob, lb = attention.sparse_attention(cb, q, "bf16", [0], bt, idx, 0.1 * 0.25)
+    np.testing.assert_allclose(oa, 0.5 * ob, rtol=1e-12)
+    np.testing.assert_allclose(la, lb, rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# split-K partitions and merge
+# ---------------------------------------------------------------------------
+
+def test_partition_rule():
+    b = attention.partition_bounds(2051, 8)
+    sizes = [e - s for s, e in b]
+    assert sizes == [257] * 7 + [252]
+    assert attention.partition_bounds(5, 8)[5:] == [(5, 5)] * 3
+    assert sum(e - s for s, e in attention.partition_bounds(1024, 16)) == 1024
+
+
+@pytest.mark.parametrize("P", [1, 2, 8, 16, 64])
+def test_merge_of_partials_equals_full(P):
+    w = wl.tiny()
+    c = _oracle_cache(w, "int8")
+    q = _src_np(w.q)
+    out, lse = attention.sparse_attention(c, q, "bf16", w.row_seq, w.block_table, w.topk_idx,
+                                          w.sm_scale)
+    parts_o, parts_l = [], []
+    for s, e in attention.partition_bounds(w.topk, P):
+        idx = np.full_like(w.topk_idx, -1)
+        idx[:, s:e] = w.topk_idx[:, s:e]
+        o, l = attention.sparse_attention(c, q, "bf16", w.row_seq, w.block_table, idx, w.sm_scale)
+        parts_o.append(o)
+        parts_l.append(l)
+    mo, ml = attention.merge_partials(parts_o, parts_l)
+    np.testing.assert_allclose(mo, out, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(ml, lse, rtol=1e-12)
+
+
+def test_tolerance_helper():
+    ref = np.array([0.0, 1.0, -10.0])
+    assert attention.within_tolerance(ref + [1.9e-3, 1.1e-2, 0.1], ref).all()
+    assert not attention.within_tolerance(ref + [2.1e-3, 0, 0], ref).all()
+    m = attention.metrics(ref * 1.01, ref)
+    assert m["cosine"] == pytest.approx(1.0)
+    assert m["rel_l2"] == pytest.approx(0.01)
