@@ -1,0 +1,260 @@
+// C ABI layer: host-side validation and dispatch.  Every check runs before
+// any HIP call; kernels are enqueued on the caller's stream and nothing here
+// synchronizes or allocates.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <limits>
+
+#include "../../include/qsakv.h"
+#include "qsakv_internal.h"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+constexpr int64_t kI64Max = std::numeric_limits<int64_t>::max();
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int log2i(int64_t x) {
+  int l = 0;
+  while ((int64_t(1) << l) < x) ++l;
+  return l;
+}
+
+// a * b without signed overflow; false if it would exceed kI64Max
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > kI64Max / a) return false;
+  *out = a * b;
+  return true;
+}
+
+bool scale_ok(float s) { return std::isfinite(s) && s >= std::numeric_limits<float>::min(); }
+
+int64_t row_bytes(int kind, int64_t d) {
+  switch (kind) {
+    case QKV_CACHE_INT8: return d;
+    case QKV_CACHE_INT8_INLINE: return d + 4;
+    case QKV_CACHE_E4M3: return d;
+    default: return 2 * d;
+  }
+}
+
+// Checks shared by every call that touches a cache.
+qkv_status check_cache(const qkv_cache* c, bool need_data) {
+  if (!c) return QKV_ERR_NULL;
+  if (c->kind < QKV_CACHE_INT8 || c->kind > QKV_CACHE_BF16) return QKV_ERR_UNSUPPORTED;
+  if (c->num_blocks <= 0 || c->num_kv_heads <= 0 || c->reserved != 0) return QKV_ERR_BAD_SHAPE;
+  if (!is_pow2(c->block_size) || c->block_size > 1024) return QKV_ERR_BAD_SHAPE;
+  if (c->head_dim != 128 && c->head_dim != 256) return QKV_ERR_UNSUPPORTED;
+  int64_t slots, t;
+  if (!mul_ok(c->num_blocks, c->block_size, &slots) || slots > INT32_MAX) return QKV_ERR_BAD_SHAPE;
+  if (!mul_ok(slots, c->num_kv_heads, &t) || !mul_ok(t, row_bytes(c->kind, c->head_dim), &t))
+    return QKV_ERR_BAD_SHAPE;
+  if (need_data) {
+    if (!c->k || !c->v) return QKV_ERR_NULL;
+    if (c->kind == QKV_CACHE_INT8 && !c->kv_scale) return QKV_ERR_NULL;
+    const uintptr_t a = c->kind == QKV_CACHE_INT8_INLINE ? 4 : 16;
+    if (!aligned(c->k, a) || !aligned(c->v, a)) return QKV_ERR_ALIGNMENT;
+    if (c->kind == QKV_CACHE_INT8 && !aligned(c->kv_scale, 8)) return QKV_ERR_ALIGNMENT;
+  }
+  if (c->kind == QKV_CACHE_E4M3 && (!scale_ok(c->k_scale) || !scale_ok(c->v_scale)))
+    return QKV_ERR_BAD_SCALE;
+  return QKV_OK;
+}
+
+qkv_status finish(hipError_t e) {
+  if (e != hipSuccess) {
+    g_last_hip_error = (int32_t)e;
+    return QKV_ERR_HIP;
+  }
+  return QKV_OK;
+}
+
+qkv_status check_args(const qkv_cache* c, const qsa_args* a) {
+  if (!a) return QKV_ERR_NULL;
+  if (a->num_rows < 0 || a->num_q_heads <= 0 || a->num_seqs <= 0 || a->block_table_stride <= 0 ||
+      a->topk <= 0)
+    return QKV_ERR_BAD_SHAPE;
+  if (a->num_q_heads % c->num_kv_heads != 0) return QKV_ERR_BAD_SHAPE;
+  const int group = a->num_q_heads / c->num_kv_heads;
+  if (group > 16) return QKV_ERR_UNSUPPORTED;
+  if (a->q_dtype != QKV_BF16 && a->q_dtype != QKV_FP16) return QKV_ERR_UNSUPPORTED;
+  if (c->kind == QKV_CACHE_BF16 && a->q_dtype != QKV_BF16) return QKV_ERR_UNSUPPORTED;
+  if (a->out_dtype != QKV_BF16 && a->out_dtype != QKV_FP16 && a->out_dtype != QKV_FP32)
+    return QKV_ERR_UNSUPPORTED;
+  if (!std::isfinite(a->sm_scale)) return QKV_ERR_BAD_SCALE;
+  int64_t t;
+  if (!mul_ok(a->num_rows, a->num_q_heads, &t) || t > INT32_MAX) return QKV_ERR_BAD_SHAPE;
+  if (!mul_ok(a->num_rows, a->topk, &t) || t > INT32_MAX) return QKV_ERR_BAD_SHAPE;
+  if (!mul_ok(a->num_seqs, a->block_table_stride, &t) || t > INT32_MAX) return QKV_ERR_BAD_SHAPE;
+  if (a->num_rows == 0) return QKV_OK;
+  if (!a->q || !a->out || !a->row_seq || !a->block_table || !a->topk_idx) return QKV_ERR_NULL;
+  if (!aligned(a->q, 16) || !aligned(a->out, 16) || !aligned(a->row_seq, 4) ||
+      !aligned(a->block_table, 4) || !aligned(a->topk_idx, 4) ||
+      (a->lse && !aligned(a->lse, 4)))
+    return QKV_ERR_ALIGNMENT;
+  return QKV_OK;
+}
+
+qsakv::AttnParams make_params(const qkv_cache* c, const qsa_args* a, int32_t splits) {
+  qsakv::AttnParams p{};
+  p.q = a->q;
+  p.row_seq = a->row_seq;
+  p.block_table = a->block_table;
+  p.topk_idx = a->topk_idx;
+  p.out = a->out;
+  p.lse = a->lse;
+  p.k = static_cast<const uint8_t*>(c->k);
+  p.v = static_cast<const uint8_t*>(c->v);
+  p.kv_scale = c->kv_scale;
+  p.sm_log2e = (float)((double)a->sm_scale * 1.4426950408889634);
+  p.k_scale = c->kind == QKV_CACHE_E4M3 ? c->k_scale : 1.f;
+  p.v_scale = c->kind == QKV_CACHE_E4M3 ? c->v_scale : 1.f;
+  p.q_dtype = a->q_dtype;
+  p.out_dtype = a->out_dtype;
+  p.num_rows = a->num_rows;
+  p.num_q_heads = a->num_q_heads;
+  p.num_kv_heads = c->num_kv_heads;
+  p.group = a->num_q_heads / c->num_kv_heads;
+  p.num_seqs = a->num_seqs;
+  p.bt_stride = a->block_table_stride;
+  p.topk = a->topk;
+  p.num_blocks = c->num_blocks;
+  p.log2_bs = log2i(c->block_size);
+  p.num_splits = splits;
+  p.chunk = (a->topk + splits - 1) / splits;
+  return p;
+}
+
+size_t ws_bytes(int64_t rows, int64_t heads, int64_t d, int64_t splits) {
+  if (rows < 0 || heads <= 0 || (d != 128 && d != 256) || splits < 1 || splits > 64) return 0;
+  if (splits == 1) return 0;
+  int64_t n;
+  if (!mul_ok(rows, heads, &n) || !mul_ok(n, splits, &n)) return 0;
+  int64_t o_bytes, ml_bytes;
+  if (!mul_ok(n, d * 4, &o_bytes) || !mul_ok(n, 8, &ml_bytes)) return 0;
+  o_bytes = (o_bytes + 255) / 256 * 256;
+  if (o_bytes > kI64Max - ml_bytes) return 0;
+  return (size_t)(o_bytes + ml_bytes);
+}
+
+}  // namespace
+
+extern "C" {
+
+qkv_status kv_quant_write(const qkv_cache* cache, const void* k_src, const void* v_src,
+                          int32_t src_dtype, int64_t num_tokens, const int64_t* slot_mapping,
+                          void* stream) {
+  qkv_status st = check_cache(cache, true);
+  if (st != QKV_OK) return st;
+  if (num_tokens < 0) return QKV_ERR_BAD_SHAPE;
+  if (src_dtype != QKV_FP32 && src_dtype != QKV_BF16 && src_dtype != QKV_FP16)
+    return QKV_ERR_UNSUPPORTED;
+  int64_t t;
+  if (!mul_ok(num_tokens, (int64_t)cache->num_kv_heads * cache->head_dim * 4, &t))
+    return QKV_ERR_BAD_SHAPE;
+  if (num_tokens == 0) return QKV_OK;
+  if (!k_src || !v_src || !slot_mapping) return QKV_ERR_NULL;
+  if (!aligned(k_src, 16) || !aligned(v_src, 16) || !aligned(slot_mapping, 8))
+    return QKV_ERR_ALIGNMENT;
+  qsakv::WriteParams p{};
+  p.k_src = k_src;
+  p.v_src = v_src;
+  p.slot_mapping = slot_mapping;
+  p.k = static_cast<uint8_t*>(cache->k);
+  p.v = static_cast<uint8_t*>(cache->v);
+  p.kv_scale = cache->kv_scale;
+  p.k_scale = cache->k_scale;
+  p.v_scale = cache->v_scale;
+  p.num_tokens = num_tokens;
+  p.num_slots = (int64_t)cache->num_blocks * cache->block_size;
+  p.num_kv_heads = cache->num_kv_heads;
+  p.src_dtype = src_dtype;
+  return finish(qsakv::launch_kv_write(cache->kind, cache->head_dim, p,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+qkv_status qsa_sparse_attn_prefill(const qkv_cache* cache, const qsa_args* args, void* stream) {
+  qkv_status st = check_cache(cache, true);
+  if (st != QKV_OK) return st;
+  st = check_args(cache, args);
+  if (st != QKV_OK || args->num_rows == 0) return st;
+  const qsakv::AttnParams p = make_params(cache, args, 1);
+  return finish(qsakv::launch_attn(cache->kind, cache->head_dim, p,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+size_t qsa_decode_workspace_bytes(int32_t num_rows, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t num_splits) {
+  return ws_bytes(num_rows, num_q_heads, head_dim, num_splits);
+}
+
+qkv_status qsa_sparse_attn_decode(const qkv_cache* cache, const qsa_args* args, int32_t num_splits,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  qkv_status st = check_cache(cache, true);
+  if (st != QKV_OK) return st;
+  st = check_args(cache, args);
+  if (st != QKV_OK) return st;
+  if (num_splits < 1 || num_splits > 64) return QKV_ERR_UNSUPPORTED;
+  int64_t items;
+  if (!mul_ok((int64_t)args->num_rows * cache->num_kv_heads, num_splits, &items) ||
+      items > INT32_MAX)
+    return QKV_ERR_BAD_SHAPE;
+  if (args->num_rows == 0) return QKV_OK;
+  qsakv::AttnParams p = make_params(cache, args, num_splits);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (num_splits == 1)
+    return finish(qsakv::launch_attn(cache->kind, cache->head_dim, p, s));
+  const size_t need = ws_bytes(args->num_rows, args->num_q_heads, cache->head_dim, num_splits);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return QKV_ERR_WORKSPACE;
+  const int64_t n = (int64_t)args->num_rows * args->num_q_heads * num_splits;
+  const int64_t o_bytes = (n * cache->head_dim * 4 + 255) / 256 * 256;
+  p.ws_o = static_cast<float*>(workspace);
+  p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+  hipError_t e = qsakv::launch_attn(cache->kind, cache->head_dim, p, s);
+  if (e != hipSuccess) return finish(e);
+  return finish(qsakv::launch_merge(cache->head_dim, p, s));
+}
+
+qkv_status qkv_cache_bytes(int32_t kind, int32_t num_blocks, int32_t block_size,
+                           int32_t num_kv_heads, int32_t head_dim, size_t* k_bytes,
+                           size_t* v_bytes, size_t* scale_bytes) {
+  if (kind < QKV_CACHE_INT8 || kind > QKV_CACHE_BF16) return QKV_ERR_UNSUPPORTED;
+  if (head_dim != 128 && head_dim != 256) return QKV_ERR_UNSUPPORTED;
+  if (num_blocks <= 0 || num_kv_heads <= 0 || !is_pow2(block_size) || block_size > 1024)
+    return QKV_ERR_BAD_SHAPE;
+  int64_t rows, kb, sb = 0;
+  if (!mul_ok((int64_t)num_blocks * block_size, num_kv_heads, &rows) ||
+      !mul_ok(rows, row_bytes(kind, head_dim), &kb))
+    return QKV_ERR_BAD_SHAPE;
+  if (kind == QKV_CACHE_INT8 && !mul_ok(rows, 8, &sb)) return QKV_ERR_BAD_SHAPE;
+  if (k_bytes) *k_bytes = (size_t)kb;
+  if (v_bytes) *v_bytes = (size_t)kb;
+  if (scale_bytes) *scale_bytes = (size_t)sb;
+  return QKV_OK;
+}
+
+const char* qkv_status_str(int32_t status) {
+  switch (status) {
+    case QKV_OK: return "QKV_OK";
+    case QKV_ERR_NULL: return "QKV_ERR_NULL: a required pointer is NULL";
+    case QKV_ERR_BAD_SHAPE: return "QKV_ERR_BAD_SHAPE: invalid or inconsistent size";
+    case QKV_ERR_UNSUPPORTED: return "QKV_ERR_UNSUPPORTED: configuration outside the supported set";
+    case QKV_ERR_BAD_SCALE: return "QKV_ERR_BAD_SCALE: scale missing, non-finite or not positive";
+    case QKV_ERR_WORKSPACE: return "QKV_ERR_WORKSPACE: split-K workspace missing, small or misaligned";
+    case QKV_ERR_HIP: return "QKV_ERR_HIP: the HIP runtime reported an error";
+    case QKV_ERR_ALIGNMENT: return "QKV_ERR_ALIGNMENT: device pointer misaligned";
+    default: return "unknown qkv_status";
+  }
+}
+
+int32_t qkv_last_hip_error(void) { return g_last_hip_error; }
+
+int32_t qkv_abi_version(void) { return QSAKV_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,116 @@
+// Device-side helpers shared by the qsakv kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qsakv {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+template <typename T>
+__device__ __forceinline__ T bitcast(const auto& x) { return __builtin_bit_cast(T, x); }
+
+// ---------------------------------------------------------------------------
+// wave reductions (shuffle based; used outside the hot loop or on few values)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+// reduce across the four 16-lane groups that share lane & 15
+__device__ __forceinline__ float group4_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float group4_sum(float x) {
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
+}
+
+// ---------------------------------------------------------------------------
+// exact conversions of cache codes to MFMA operands
+// ---------------------------------------------------------------------------
+// Byte permute: result byte k = byte sel.k of the 8-byte value {hi, lo}
+// (selector 0..3 -> lo bytes, 4..7 -> hi bytes).
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// Two signed int8 codes in bytes (b_lo, b_hi) of `x` -- already XOR-ed with
+// 0x80 so that each byte holds q + 128 -- become the fp16 pair
+// (q_lo, q_hi): 0x64XX is the fp16 value 1024 + XX, exact for XX < 256, and
+// subtracting 1152 leaves q exactly (|q| <= 127 fits fp16's 11-bit
+// significand).
+__device__ __forceinline__ uint32_t i8pair_to_f16x2(uint32_t x_biased, uint32_t sel) {
+  return perm(0x64646464u, x_biased, sel);
+}
+constexpr uint32_t kSelB01 = 0x04010400u;  // bytes 0,1 -> (0x64b0, 0x64b1)
+constexpr uint32_t kSelB23 = 0x04030402u;  // bytes 2,3 -> (0x64b2, 0x64b3)
+
+__device__ __forceinline__ f16x8 sub1152(u32x4 w) {
+  const f16x8 bias = {1152, 1152, 1152, 1152, 1152, 1152, 1152, 1152};
+  return bitcast<f16x8>(w) - bias;
+}
+
+// Eight int8 codes (two little-endian words, element order preserved) ->
+// eight exact fp16 values.
+__device__ __forceinline__ f16x8 i8x8_to_f16(uint32_t w0, uint32_t w1) {
+  const uint32_t x0 = w0 ^ 0x80808080u, x1 = w1 ^ 0x80808080u;
+  u32x4 r;
+  r[0] = i8pair_to_f16x2(x0, kSelB01);
+  r[1] = i8pair_to_f16x2(x0, kSelB23);
+  r[2] = i8pair_to_f16x2(x1, kSelB01);
+  r[3] = i8pair_to_f16x2(x1, kSelB23);
+  return sub1152(r);
+}
+
+// Two OCP E4M3FN codes in the low (hi_word = false) or high 16 bits of w ->
+// two exact fp16 values (every E4M3 value is representable in fp16), using
+// gfx950's OCP-FP8 conversion with unit scale.
+template <bool kHiWord>
+__device__ __forceinline__ uint32_t e4m3pair_to_f16x2(uint32_t w) {
+  f16x2 h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, kHiWord);
+  return bitcast<uint32_t>(h);
+}
+__device__ __forceinline__ f16x8 e4m3x8_to_f16(uint32_t w0, uint32_t w1) {
+  u32x4 r;
+  r[0] = e4m3pair_to_f16x2<false>(w0);
+  r[1] = e4m3pair_to_f16x2<true>(w0);
+  r[2] = e4m3pair_to_f16x2<false>(w1);
+  r[3] = e4m3pair_to_f16x2<true>(w1);
+  return bitcast<f16x8>(r);
+}
+
+// ---------------------------------------------------------------------------
+// MFMA 16x16x32 (fp16 / bf16 inputs, fp32 accumulate)
+//   A (16 x 32): lane l holds row l%16, k-slots 8*(l/16) .. +7
+//   B (32 x 16): lane l holds col l%16, the same k-slots
+//   C (16 x 16): lane l holds rows 4*(l/16) .. +3 of col l%16
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x4 mfma16(const f16x8& a, const f16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+}  // namespace qsakv

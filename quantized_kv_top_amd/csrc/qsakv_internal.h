@@ -1,0 +1,66 @@
+// Host-side launch interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qsakv {
+
+enum Kind : int { kInt8 = 0, kInt8Inline = 1, kE4M3 = 2, kBF16 = 3 };
+enum DType : int { kDtBF16 = 0, kDtFP16 = 1, kDtFP32 = 2 };
+
+// Everything a write kernel needs; validated by the caller.
+struct WriteParams {
+  const void* k_src;
+  const void* v_src;
+  const int64_t* slot_mapping;
+  uint8_t* k;
+  uint8_t* v;
+  float* kv_scale;
+  float k_scale;          // E4M3 only
+  float v_scale;
+  int64_t num_tokens;
+  int64_t num_slots;      // NB * BS
+  int32_t num_kv_heads;
+  int32_t src_dtype;
+};
+
+hipError_t launch_kv_write(int kind, int head_dim, const WriteParams& p, hipStream_t s);
+
+// Everything an attention kernel needs; validated by the caller.
+struct AttnParams {
+  const void* q;
+  const int32_t* row_seq;
+  const int32_t* block_table;
+  const int32_t* topk_idx;
+  void* out;
+  float* lse;             // may be null
+  const uint8_t* k;
+  const uint8_t* v;
+  const float* kv_scale;  // INT8 side layout
+  float* ws_o;            // split-K partials [R][Hq][P][D]   (P > 1)
+  float* ws_ml;           // split-K (max, sum) [R][Hq][P][2] (P > 1)
+  float sm_log2e;         // sm_scale * log2(e)
+  float k_scale;          // E4M3 per-layer scales (1 otherwise)
+  float v_scale;
+  int32_t q_dtype;
+  int32_t out_dtype;
+  int32_t num_rows;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;          // Hq / Hkv
+  int32_t num_seqs;
+  int32_t bt_stride;
+  int32_t topk;
+  int32_t num_blocks;
+  int32_t log2_bs;
+  int32_t num_splits;     // P
+  int32_t chunk;          // ceil(topk / P)
+};
+
+// One pass over every (row, KV head, partition); P == 1 writes out/lse,
+// P > 1 writes the partials, then launch_merge combines them.
+hipError_t launch_attn(int kind, int head_dim, const AttnParams& p, hipStream_t s);
+hipError_t launch_merge(int head_dim, const AttnParams& p, hipStream_t s);
+
+}  // namespace qsakv

@@ -1,0 +1,200 @@
+"""Thin ctypes binding of the qsakv C ABI (``include/qsakv.h``).
+
+Argument marshalling only: every step of the path runs in the HIP library.
+PyTorch supplies device memory and streams.  The library must be built
+(``python -m quantized_kv_top_amd.build``); loading fails loudly otherwise.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libqsakv.so")
+
+# status codes (qkv_status)
+OK, ERR_NULL, ERR_BAD_SHAPE, ERR_UNSUPPORTED, ERR_BAD_SCALE, ERR_WORKSPACE, ERR_HIP, \
+    ERR_ALIGNMENT = range(8)
+# dtypes (qkv_dtype)
+BF16, FP16, FP32 = 0, 1, 2
+# cache kinds (qkv_cache_kind)
+CACHE_INT8, CACHE_INT8_INLINE, CACHE_E4M3, CACHE_BF16 = 0, 1, 2, 3
+KIND_BY_NAME = {"int8": CACHE_INT8, "int8_inline": CACHE_INT8_INLINE,
+                "e4m3": CACHE_E4M3, "bf16": CACHE_BF16}
+
+EXPORTED = ("kv_quant_write", "qsa_sparse_attn_prefill", "qsa_decode_workspace_bytes",
+            "qsa_sparse_attn_decode", "qkv_cache_bytes", "qkv_status_str",
+            "qkv_last_hip_error", "qkv_abi_version")
+
+
+class QkvCache(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("kv_scale", ctypes.c_void_p), ("k_scale", ctypes.c_float),
+                ("v_scale", ctypes.c_float)]
+
+
+class QsaArgs(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("q_dtype", ctypes.c_int32),
+                ("num_rows", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_seqs", ctypes.c_int32), ("row_seq", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("block_table_stride", ctypes.c_int32),
+                ("topk", ctypes.c_int32), ("topk_idx", ctypes.c_void_p),
+                ("sm_scale", ctypes.c_float), ("out_dtype", ctypes.c_int32),
+                ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libqsakv.so (once) and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("qsakv: %s is not built; run `python -m quantized_kv_top_amd.build`"
+                           % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    c_i32, c_i64, c_sz, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+    P = ctypes.POINTER
+    L.kv_quant_write.argtypes = [P(QkvCache), c_vp, c_vp, c_i32, c_i64, c_vp, c_vp]
+    L.kv_quant_write.restype = c_i32
+    L.qsa_sparse_attn_prefill.argtypes = [P(QkvCache), P(QsaArgs), c_vp]
+    L.qsa_sparse_attn_prefill.restype = c_i32
+    L.qsa_decode_workspace_bytes.argtypes = [c_i32, c_i32, c_i32, c_i32]
+    L.qsa_decode_workspace_bytes.restype = c_sz
+    L.qsa_sparse_attn_decode.argtypes = [P(QkvCache), P(QsaArgs), c_i32, c_vp, c_sz, c_vp]
+    L.qsa_sparse_attn_decode.restype = c_i32
+    L.qkv_cache_bytes.argtypes = [c_i32, c_i32, c_i32, c_i32, c_i32, P(c_sz), P(c_sz), P(c_sz)]
+    L.qkv_cache_bytes.restype = c_i32
+    L.qkv_status_str.argtypes = [c_i32]
+    L.qkv_status_str.restype = ctypes.c_char_p
+    L.qkv_last_hip_error.argtypes = []
+    L.qkv_last_hip_error.restype = c_i32
+    L.qkv_abi_version.argtypes = []
+    L.qkv_abi_version.restype = c_i32
+    _lib = L
+    return L
+
+
+class QsakvError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = lib().qkv_status_str(status).decode()
+        if status == ERR_HIP:
+            msg += " (hipError %d)" % lib().qkv_last_hip_error()
+        super().__init__("%s: %s" % (where, msg))
+
+
+def _check(status, where):
+    if status != OK:
+        raise QsakvError(status, where)
+
+
+_DT = {torch.bfloat16: BF16, torch.float16: FP16, torch.float32: FP32}
+
+
+def dtype_code(t):
+    return _DT[t.dtype]
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def cache_bytes(kind, num_blocks, block_size, num_kv_heads, head_dim):
+    """(k_bytes, v_bytes, scale_bytes) of a cache, from the library."""
+    kb, vb, sb = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().qkv_cache_bytes(KIND_BY_NAME.get(kind, kind), num_blocks, block_size,
+                                 num_kv_heads, head_dim, ctypes.byref(kb), ctypes.byref(vb),
+                                 ctypes.byref(sb)), "qkv_cache_bytes")
+    return kb.value, vb.value, sb.value
+
+
+class Cache:
+    """One layer's paged cache: device tensors plus the descriptor.
+
+    ``k``/``v`` are uint8 tensors of the layout's bytes; ``kv_scale`` is the
+    float32 side tensor (int8 kind) or None; ``k_scale``/``v_scale`` are the
+    per-layer E4M3 scales (host floats).
+    """
+
+    def __init__(self, kind, num_blocks, block_size, num_kv_heads, head_dim, device="cuda",
+                 k_scale=1.0, v_scale=1.0, zero=True):
+        self.kind = kind
+        self.kind_code = KIND_BY_NAME[kind]
+        self.num_blocks, self.block_size = num_blocks, block_size
+        self.num_kv_heads, self.head_dim = num_kv_heads, head_dim
+        kb, vb, sb = cache_bytes(kind, num_blocks, block_size, num_kv_heads, head_dim)
+        alloc = torch.zeros if zero else torch.empty
+        self.k = alloc(kb, dtype=torch.uint8, device=device)
+        self.v = alloc(vb, dtype=torch.uint8, device=device)
+        self.kv_scale = alloc(sb // 4, dtype=torch.float32, device=device) if sb else None
+        self.k_scale = float(k_scale)
+        self.v_scale = float(v_scale)
+
+    @property
+    def num_slots(self):
+        return self.num_blocks * self.block_size
+
+    def desc(self):
+        return QkvCache(self.kind_code, self.num_blocks, self.block_size, self.num_kv_heads,
+                        self.head_dim, 0, self.k.data_ptr(), self.v.data_ptr(),
+                        None if self.kv_scale is None else self.kv_scale.data_ptr(),
+                        self.k_scale, self.v_scale)
+
+    def nbytes(self):
+        return self.k.numel() + self.v.numel() + (0 if self.kv_scale is None else
+                                                  4 * self.kv_scale.numel())
+
+
+def kv_quant_write(cache, k_src, v_src, slot_mapping, stream=None):
+    """Quantize-on-write ``k_src``/``v_src`` [T][Hkv][D] into ``cache`` at
+    ``slot_mapping`` [T] (int64; < 0 skips)."""
+    d = cache.desc()
+    T = k_src.shape[0]
+    _check(lib().kv_quant_write(ctypes.byref(d), _ptr(k_src), _ptr(v_src), dtype_code(k_src), T,
+                                _ptr(slot_mapping), _stream(stream)), "kv_quant_write")
+
+
+def _args(q, row_seq, block_table, topk_idx, sm_scale, out, lse):
+    R, Hq, _ = q.shape
+    return QsaArgs(q.data_ptr(), dtype_code(q), R, Hq, block_table.shape[0], row_seq.data_ptr(),
+                   block_table.data_ptr(), block_table.shape[1], topk_idx.shape[1],
+                   topk_idx.data_ptr(), float(sm_scale), dtype_code(out), out.data_ptr(),
+                   None if lse is None else lse.data_ptr())
+
+
+def qsa_sparse_attn_prefill(cache, q, row_seq, block_table, topk_idx, sm_scale, out, lse=None,
+                            stream=None):
+    """Single-pass sparse attention; writes ``out`` [R][Hq][D] and ``lse`` [R][Hq]."""
+    d = cache.desc()
+    a = _args(q, row_seq, block_table, topk_idx, sm_scale, out, lse)
+    _check(lib().qsa_sparse_attn_prefill(ctypes.byref(d), ctypes.byref(a), _stream(stream)),
+           "qsa_sparse_attn_prefill")
+
+
+def qsa_decode_workspace_bytes(num_rows, num_q_heads, head_dim, num_splits):
+    return lib().qsa_decode_workspace_bytes(num_rows, num_q_heads, head_dim, num_splits)
+
+
+def qsa_sparse_attn_decode(cache, q, row_seq, block_table, topk_idx, sm_scale, out, num_splits,
+                           workspace, lse=None, stream=None):
+    """Split-K sparse attention with log-sum-exp merge; ``workspace`` is a
+    uint8 device tensor of at least qsa_decode_workspace_bytes(...) bytes."""
+    d = cache.desc()
+    a = _args(q, row_seq, block_table, topk_idx, sm_scale, out, lse)
+    wp = None if workspace is None else ctypes.c_void_p(workspace.data_ptr())
+    wb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().qsa_sparse_attn_decode(ctypes.byref(d), ctypes.byref(a), num_splits, wp, wb,
+                                        _stream(stream)), "qsa_sparse_attn_decode")

@@ -1,0 +1,159 @@
+"""Host-side checks of the C ABI: the library loads, exports what the header
+declares, sizes caches and workspaces by the closed forms, and rejects bad
+arguments before any HIP call.  No GPU: every call here returns from host
+validation (dummy device pointers are never dereferenced)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from oracle import cache as ocache
+from quantized_kv_top_amd import qsakv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qsakv.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(qsakv.LIB_PATH),
+                                reason="libqsakv.so not built")
+
+DUMMY = 0x10000          # 64 KiB: 256-byte aligned, never dereferenced on these paths
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*QSAKV_API\s+(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_exports_every_declared_function():
+    names = header_functions()
+    assert set(names) == set(qsakv.EXPORTED)
+    L = qsakv.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.qkv_abi_version() == 1
+
+
+def test_struct_layouts():
+    # int32 x 6, then pointers: offsets follow the C ABI
+    assert qsakv.QkvCache.k.offset == 24
+    assert qsakv.QkvCache.k_scale.offset == 48
+    assert ctypes.sizeof(qsakv.QkvCache) == 56
+    assert qsakv.QsaArgs.row_seq.offset == 24
+    assert ctypes.sizeof(qsakv.QsaArgs) == 80
+
+
+@pytest.mark.parametrize("kind", ocache.KINDS)
+@pytest.mark.parametrize("D", [128, 256])
+def test_cache_bytes_match_oracle_layout(kind, D):
+    NB, BS, H = 37, 64, 2
+    kb, vb, sb = qsakv.cache_bytes(kind, NB, BS, H, D)
+    assert kb == vb == NB * BS * H * ocache.row_bytes(kind, D)
+    per_token = (kb + vb + sb) // (NB * BS)
+    assert per_token == ocache.bytes_per_token(kind, H, D)
+
+
+def test_workspace_bytes():
+    L = qsakv.lib()
+    n = 40 * 16 * 8
+    assert L.qsa_decode_workspace_bytes(40, 16, 256, 8) == n * 256 * 4 + n * 8
+    assert L.qsa_decode_workspace_bytes(40, 16, 256, 1) == 0
+    assert L.qsa_decode_workspace_bytes(40, 16, 64, 8) == 0
+    assert L.qsa_decode_workspace_bytes(40, 16, 256, 65) == 0
+
+
+def _cache(kind="int8", NB=8, BS=16, H=1, D=128, ks=1.0, vs=1.0, scale_ptr=DUMMY):
+    return qsakv.QkvCache(qsakv.KIND_BY_NAME[kind], NB, BS, H, D, 0, DUMMY, DUMMY,
+                          scale_ptr, ks, vs)
+
+
+def _args(R=4, Hq=4, topk=16, q_dtype=qsakv.BF16, out_dtype=qsakv.FP32, sm=0.125, q=DUMMY):
+    return qsakv.QsaArgs(q, q_dtype, R, Hq, 1, DUMMY, DUMMY, 4, topk, DUMMY, sm, out_dtype,
+                         DUMMY, None)
+
+
+def _prefill(c, a):
+    return qsakv.lib().qsa_sparse_attn_prefill(ctypes.byref(c), ctypes.byref(a), None)
+
+
+def _decode(c, a, P=8, ws=DUMMY, wsb=1 << 30):
+    return qsakv.lib().qsa_sparse_attn_decode(ctypes.byref(c), ctypes.byref(a), P, ws, wsb, None)
+
+
+def _write(c, T=4, dt=qsakv.FP32, k=DUMMY):
+    return qsakv.lib().kv_quant_write(ctypes.byref(c), k, DUMMY, dt, T, DUMMY, None)
+
+
+def test_null_pointers():
+    L = qsakv.lib()
+    assert L.qsa_sparse_attn_prefill(None, ctypes.byref(_args()), None) == qsakv.ERR_NULL
+    assert L.qsa_sparse_attn_prefill(ctypes.byref(_cache()), None, None) == qsakv.ERR_NULL
+    assert _write(_cache(), k=None) == qsakv.ERR_NULL
+    assert _prefill(_cache(scale_ptr=None), _args()) == qsakv.ERR_NULL
+    assert _prefill(_cache(), _args(q=None)) == qsakv.ERR_NULL
+
+
+def test_shapes_and_supported_set():
+    assert _prefill(_cache(D=64), _args()) == qsakv.ERR_UNSUPPORTED
+    assert _prefill(_cache(BS=48), _args()) == qsakv.ERR_BAD_SHAPE
+    assert _prefill(_cache(BS=2048), _args()) == qsakv.ERR_BAD_SHAPE
+    assert _prefill(_cache(H=3), _args(Hq=4)) == qsakv.ERR_BAD_SHAPE
+    assert _prefill(_cache(H=1), _args(Hq=32)) == qsakv.ERR_UNSUPPORTED
+    assert _prefill(_cache(), _args(topk=0)) == qsakv.ERR_BAD_SHAPE
+    assert _prefill(_cache(), _args(R=-1)) == qsakv.ERR_BAD_SHAPE
+    assert _prefill(_cache(), _args(q_dtype=qsakv.FP32)) == qsakv.ERR_UNSUPPORTED
+    assert _prefill(_cache(kind="bf16"), _args(q_dtype=qsakv.FP16)) == qsakv.ERR_UNSUPPORTED
+    assert _prefill(_cache(), _args(out_dtype=7)) == qsakv.ERR_UNSUPPORTED
+    bad = _cache()
+    bad.kind = 9
+    assert _prefill(bad, _args()) == qsakv.ERR_UNSUPPORTED
+    assert _write(_cache(), T=-1) == qsakv.ERR_BAD_SHAPE
+    assert _write(_cache(), dt=5) == qsakv.ERR_UNSUPPORTED
+
+
+def test_fail_closed_scales():
+    """E4M3 scales must be explicit, finite and positive; 1.0 is legal."""
+    for ks in [float("nan"), float("inf"), 0.0, -1.0, 1e-40]:
+        assert _prefill(_cache("e4m3", ks=ks), _args()) == qsakv.ERR_BAD_SCALE
+        assert _prefill(_cache("e4m3", vs=ks), _args()) == qsakv.ERR_BAD_SCALE
+        assert _write(_cache("e4m3", ks=ks)) == qsakv.ERR_BAD_SCALE
+    assert _prefill(_cache(), _args(sm=float("nan"))) == qsakv.ERR_BAD_SCALE
+    # unit scale passes validation (checked with a zero-row call: no launch)
+    assert _prefill(_cache("e4m3", ks=1.0, vs=1.0), _args(R=0)) == qsakv.OK
+    # int8 caches ignore k_scale / v_scale entirely
+    assert _prefill(_cache("int8", ks=float("nan")), _args(R=0)) == qsakv.OK
+
+
+def test_alignment():
+    assert _prefill(_cache(), _args(q=DUMMY + 4)) == qsakv.ERR_ALIGNMENT
+    c = _cache()
+    c.k = DUMMY + 8
+    assert _prefill(c, _args()) == qsakv.ERR_ALIGNMENT
+    c = _cache("int8_inline")
+    c.k = DUMMY + 4          # inline rows are 4-byte aligned by construction
+    assert _prefill(c, _args(R=0)) == qsakv.OK
+    assert _decode(_cache(), _args(), ws=DUMMY + 16) == qsakv.ERR_WORKSPACE
+
+
+def test_decode_splits_and_workspace():
+    assert _decode(_cache(), _args(), P=0) == qsakv.ERR_UNSUPPORTED
+    assert _decode(_cache(), _args(), P=65) == qsakv.ERR_UNSUPPORTED
+    assert _decode(_cache(), _args(), ws=None) == qsakv.ERR_WORKSPACE
+    need = qsakv.lib().qsa_decode_workspace_bytes(4, 4, 128, 8)
+    assert _decode(_cache(), _args(), wsb=need - 1) == qsakv.ERR_WORKSPACE
+
+
+def test_empty_calls_are_noops():
+    assert _write(_cache(), T=0) == qsakv.OK
+    assert _prefill(_cache(), _args(R=0)) == qsakv.OK
+    assert _decode(_cache(), _args(R=0)) == qsakv.OK
+
+
+def test_status_strings():
+    L = qsakv.lib()
+    for s in range(8):
+        assert L.qkv_status_str(s).decode().startswith("QKV_")
+    assert b"unknown" in L.qkv_status_str(99)

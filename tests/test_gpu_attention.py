@@ -1,0 +1,283 @@
+"""GPU parity of the sparse-attention entry points against the fp64 oracle:
+every cache kind, prefill and split-K decode, layouts, edge cases."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import formats as ofmt
+from quantized_kv_top_amd import qsakv
+from quantized_kv_top_amd import workloads as wl
+
+from parity_util import (check, dev, e4m3_scales, gpu_write, oracle_attention, oracle_write,
+                         run_attention, say)
+
+pytestmark = pytest.mark.gpu
+
+KINDS = ["int8", "int8_inline", "e4m3", "bf16"]
+
+
+def _setup(kind, w):
+    ks, vs = e4m3_scales(w) if kind == "e4m3" else (None, None)
+    c = gpu_write(kind, w, ks or 1.0, vs or 1.0)
+    oc = oracle_write(kind, w, ks, vs)
+    return c, oc
+
+
+def small_workload(seed=7, Hq=8, Hkv=2, D=256, BS=16, ctx=700, rows=12, topk=100,
+                   q_dtype="bf16", src="bf16", pad=0):
+    """A multi-tile case with a ragged tail: ``topk`` positions per row drawn
+    from each row's causal prefix, in random order, plus ``pad`` -1 entries."""
+    rng = np.random.default_rng(seed)
+    nb = -(-ctx // BS)
+    pool = nb + 7
+    bt = wl.scattered_block_table(rng, 2, nb, 2 * nb + 11).astype(np.int32)
+    pool = 2 * nb + 11
+    T = 2 * ctx
+    slots = np.concatenate([wl.slot_mapping_for(bt, b, np.arange(ctx), BS) for b in range(2)])
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[src]
+    k = wl.normal((T, Hkv, D), seed + 1, "cpu", tdt)
+    v = wl.normal((T, Hkv, D), seed + 2, "cpu", tdt)
+    qdt = torch.bfloat16 if q_dtype == "bf16" else torch.float16
+    q = wl.normal((rows, Hq, D), seed + 3, "cpu", qdt)
+    row_seq = (np.arange(rows) % 2).astype(np.int32)
+    idx = np.full((rows, topk + pad), -1, np.int32)
+    for r in range(rows):
+        p = ctx - 1 - r
+        sel = rng.permutation(wl.draw_sorted_distinct(rng, min(topk, p + 1), 0, p))
+        idx[r, :sel.size] = sel
+        idx[r] = rng.permutation(idx[r])
+    return wl.Workload("small", Hq, Hkv, D, BS, pool, q_dtype, "fp32", src, k, v, slots, q,
+                       row_seq, bt, idx, wl.sm_scale_for(D))
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_tiny_prefill(kind):
+    w = wl.tiny()
+    c, oc = _setup(kind, w)
+    say("tiny prefill", kind)
+    o, l = run_attention(c, w)
+    ro, rl = oracle_attention(oc, w)
+    check(o, l, ro, rl, "tiny " + kind)
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("D", [128, 256])
+def test_small_multitile(kind, D):
+    w = small_workload(D=D, q_dtype="bf16", pad=9)
+    c, oc = _setup(kind, w)
+    ro, rl = oracle_attention(oc, w)
+    for od in ["fp32", "bf16", "fp16"]:
+        say("small", kind, D, od)
+        o, l = run_attention(c, w, out_dtype=od)
+        check(o, l, ro, rl, "small %s D%d %s" % (kind, D, od))
+
+
+@pytest.mark.parametrize("kind", ["int8", "int8_inline", "e4m3"])
+def test_fp16_queries(kind):
+    w = small_workload(seed=11, q_dtype="fp16", src="fp16", D=128, Hq=32, Hkv=4, topk=77)
+    c, oc = _setup(kind, w)
+    say("fp16 q", kind)
+    o, l = run_attention(c, w, out_dtype="fp16")
+    ro, rl = oracle_attention(oc, w)
+    check(o, l, ro, rl, "fp16 q " + kind)
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("P", [1, 2, 3, 8, 16, 64])
+def test_decode_splits(kind, P):
+    w = small_workload(seed=5, topk=150, rows=6)
+    c, oc = _setup(kind, w)
+    ro, rl = oracle_attention(oc, w)
+    say("decode", kind, "P", P)
+    o, l = run_attention(c, w, num_splits=P, decode=True)
+    check(o, l, ro, rl, "decode %s P%d" % (kind, P))
+
+
+@pytest.mark.parametrize("G", [1, 4, 16])
+def test_group_sizes(G):
+    w = small_workload(seed=13, Hq=2 * G, Hkv=2, D=128, topk=40)
+    c, oc = _setup("int8", w)
+    say("group", G)
+    o, l = run_attention(c, w)
+    ro, rl = oracle_attention(oc, w)
+    check(o, l, ro, rl, "G%d" % G)
+
+
+def test_layouts_give_identical_bits():
+    """The aligned side-tensor and inline-260 layouts hold the same values, so
+    the attention outputs must be bitwise equal."""
+    w = small_workload(seed=17, topk=300, rows=8)
+    a = gpu_write("int8", w)
+    b = gpu_write("int8_inline", w)
+    oa, la = run_attention(a, w, out_dtype="fp32")
+    ob, lb = run_attention(b, w, out_dtype="fp32")
+    assert np.array_equal(oa, ob) and np.array_equal(la, lb)
+
+
+def test_permuted_block_table_same_bits():
+    w = small_workload(seed=19, topk=120, rows=6)
+    a = gpu_write("int8", w)
+    oa, la = run_attention(a, w, out_dtype="fp32")
+    # move every block to a different physical block
+    rng = np.random.default_rng(3)
+    perm = rng.permutation(w.num_blocks).astype(np.int32)
+    w2 = small_workload(seed=19, topk=120, rows=6)
+    w2.block_table = perm[w2.block_table]
+    w2.slot_mapping = (perm[w2.slot_mapping // w2.block_size].astype(np.int64) * w2.block_size
+                       + w2.slot_mapping % w2.block_size)
+    b = gpu_write("int8", w2)
+    ob, lb = run_attention(b, w2, out_dtype="fp32")
+    assert np.array_equal(oa, ob) and np.array_equal(la, lb)
+
+
+def test_deterministic():
+    w = small_workload(seed=23, topk=200)
+    c = gpu_write("int8", w)
+    o1, l1 = run_attention(c, w, out_dtype="fp32")
+    o2, l2 = run_attention(c, w, out_dtype="fp32")
+    o3, l3 = run_attention(c, w, num_splits=8, out_dtype="fp32")
+    o4, l4 = run_attention(c, w, num_splits=8, out_dtype="fp32")
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    assert np.array_equal(o3, o4) and np.array_equal(l3, l4)
+
+
+def test_edge_cases():
+    """topk = 1, all-padding rows, invalid sequence ids, out-of-range
+    positions, out-of-range block-table entries, duplicates."""
+    w = small_workload(seed=29, topk=40, rows=8)
+    c, oc = _setup("int8", w)
+    idx = w.topk_idx.copy()
+    idx[0] = -1                                   # empty row
+    idx[1, 1:] = -1                               # a single position
+    idx[2, :5] = 10 ** 6                          # beyond the block table
+    idx[3, 3] = idx[3, 2]                         # a duplicate (counts twice)
+    row_seq = w.row_seq.copy()
+    row_seq[4] = 7                                # no such sequence
+    ref_idx = idx.copy()
+    ref_idx[2, :5] = -1
+    ref_rs = row_seq.copy()
+    ref_rs[4] = 0
+    ref_idx[4] = -1
+    for P in (1, 4):
+        say("edge P", P)
+        o, l = run_attention(c, w, num_splits=P, decode=P > 1, topk_idx=idx, row_seq=row_seq)
+        ro, rl = oracle_attention(oc, w, topk_idx=ref_idx, row_seq=ref_rs)
+        check(o, l, ro, rl, "edge P%d" % P)
+        assert np.all(o[0] == 0) and np.all(np.isneginf(l[0]))
+        assert np.all(o[4] == 0) and np.all(np.isneginf(l[4]))
+    # block-table entries outside the cache are padding too
+    bt = w.block_table.copy()
+    bt[0, 0] = w.num_blocks + 5
+    bt[1, 1] = -3
+    w2 = small_workload(seed=29, topk=40, rows=8)
+    w2.block_table = bt
+    o, l = run_attention(c, w2)
+    ref_idx = w2.topk_idx.copy()
+    for r in range(w2.num_rows):
+        b = w2.row_seq[r]
+        lb = ref_idx[r] // w2.block_size
+        bad = ((b == 0) & (lb == 0)) | ((b == 1) & (lb == 1))
+        ref_idx[r][bad & (ref_idx[r] >= 0)] = -1
+    ro, rl = oracle_attention(oc, w, topk_idx=ref_idx)
+    check(o, l, ro, rl, "bad block table")
+
+
+def test_equal_keys_give_uniform_softmax():
+    """Closed form through the whole HIP path: identical keys -> the output is
+    the mean of the selected values."""
+    w = small_workload(seed=31, topk=64, rows=4, D=128)
+    key = w.k_src[:1].clone()
+    w.k_src = key.expand_as(w.k_src).contiguous()
+    c, oc = _setup("int8", w)
+    o, l = run_attention(c, w, out_dtype="fp32")
+    ro, rl = oracle_attention(oc, w)
+    check(o, l, ro, rl, "equal keys")
+    slots = [w.block_table[w.row_seq[r]][p // w.block_size] * w.block_size + p % w.block_size
+             for r in range(4) for p in [w.topk_idx[r][w.topk_idx[r] >= 0]]]
+    for r in range(4):
+        vh = oc.dequant(np.asarray(slots[r], np.int64), "v")
+        G = w.num_q_heads // w.num_kv_heads
+        for h in range(w.num_q_heads):
+            mean = vh[:, h // G, :].mean(axis=0)
+            assert np.allclose(o[r, h], mean, atol=2e-3, rtol=1e-2)
+
+
+def test_zero_value_rows_and_large_queries():
+    """Zero V rows (scale 0) and bf16 queries far from unit magnitude (the
+    fp16 prescale path)."""
+    w = small_workload(seed=37, topk=90, rows=6)
+    v = w.v_src.clone()
+    v[::3] = 0
+    w.v_src = v
+    q = w.q.float()
+    q[0] *= 3e4
+    q[1] *= 1e-5
+    q[2, :, ::2] *= 1e-20
+    w.q = q.to(torch.bfloat16)
+    c, oc = _setup("int8", w)
+    o, l = run_attention(c, w, out_dtype="fp32", sm_scale=w.sm_scale * 1e-3)
+    ro, rl = oracle_attention(oc, w, sm_scale=w.sm_scale * 1e-3)
+    check(o, l, ro, rl, "zero V / large q")
+
+
+def test_every_e4m3_code_decodes_exactly():
+    """Write all 254 finite E4M3 codes as V rows directly into the cache and
+    read each back with top-k = 1: out = decode(code) * v_scale exactly."""
+    D, Hkv, BS = 128, 1, 16
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    n = codes.size
+    NB = -(-n // BS)
+    c = qsakv.Cache("e4m3", NB, BS, Hkv, D, k_scale=1.0, v_scale=0.75)
+    vrows = np.repeat(codes[:, None], D, axis=1)
+    c.v.view(NB * BS, D)[:n] = dev(vrows)
+    q = torch.zeros(n, 1, D, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty(n, 1, D, dtype=torch.float32, device="cuda")
+    lse = torch.empty(n, 1, dtype=torch.float32, device="cuda")
+    bt = dev(np.arange(NB, dtype=np.int32)[None], torch.int32)
+    idx = dev(np.arange(n, dtype=np.int32)[:, None], torch.int32)
+    rs = torch.zeros(n, dtype=torch.int32, device="cuda")
+    qsakv.qsa_sparse_attn_prefill(c, q, rs, bt, idx, 0.1, out, lse=lse)
+    torch.cuda.synchronize()
+    want = ofmt.e4m3_decode(codes) * 0.75
+    got = out.cpu().numpy()
+    assert np.array_equal(got, np.repeat(want[:, None, None], D, axis=2).astype(np.float32))
+    assert np.all(lse.cpu().numpy() == 0)
+
+
+def test_every_int8_code_decodes_exactly():
+    D, Hkv, BS = 256, 1, 16
+    codes = np.arange(-127, 128, dtype=np.int8)
+    n = codes.size
+    NB = -(-n // BS)
+    c = qsakv.Cache("int8", NB, BS, Hkv, D)
+    c.v.view(NB * BS, D)[:n] = dev(np.repeat(codes.view(np.uint8)[:, None], D, axis=1))
+    s = np.float32(0.0371)
+    c.kv_scale.view(NB * BS, 2)[:n, 1] = float(s)
+    c.kv_scale.view(NB * BS, 2)[:n, 0] = 1.0
+    q = torch.zeros(n, 1, D, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty(n, 1, D, dtype=torch.float32, device="cuda")
+    bt = dev(np.arange(NB, dtype=np.int32)[None], torch.int32)
+    idx = dev(np.arange(n, dtype=np.int32)[:, None], torch.int32)
+    rs = torch.zeros(n, dtype=torch.int32, device="cuda")
+    qsakv.qsa_sparse_attn_prefill(c, q, rs, bt, idx, 0.1, out)
+    torch.cuda.synchronize()
+    want = codes.astype(np.float64) * np.float64(s)
+    got = out.cpu().numpy()[:, 0, 0].astype(np.float64)
+    np.testing.assert_allclose(got, want, rtol=2e-7, atol=0)
+
+
+def test_e4m3_scale_folding():
+    """k_scale = c equals k_scale = 1 with sm_scale * c; v_scale = c scales
+    the output by c -- on the same stored codes."""
+    w = small_workload(seed=41, D=128, topk=120, rows=6)
+    ks, vs = e4m3_scales(w)
+    a = gpu_write("e4m3", w, ks, vs)
+    b = qsakv.Cache("e4m3", w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim,
+                    k_scale=1.0, v_scale=1.0)
+    b.k.copy_(a.k)
+    b.v.copy_(a.v)
+    oa, la = run_attention(a, w, out_dtype="fp32")
+    ob, lb = run_attention(b, w, out_dtype="fp32", sm_scale=w.sm_scale * ks)
+    np.testing.assert_allclose(oa, vs * ob, rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(la, lb, rtol=1e-5, atol=1e-5)

@@ -1,0 +1,174 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times.  Cache bytes are compared on every written token where the
+oracle can afford it, else on a seeded sample plus every token the checked
+rows attend to; attention outputs on sampled rows."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import cache as ocache
+from quantized_kv_top_amd import qsakv
+from quantized_kv_top_amd import workloads as wl
+
+from parity_util import (assert_rows_equal, check, dev, e4m3_scales, gpu_write, needed_tokens,
+                         oracle_attention, oracle_write, run_attention, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample_rows(R, n, seed):
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(4, R - 4), size=max(0, n - 8), replace=False)
+    return np.unique(np.concatenate([np.arange(4), mid, np.arange(R - 4, R)]))
+
+
+def test_prefill_full_size_both_layouts():
+    w = wl.prefill(device="cuda")
+    say("prefill full: %d rows x topk %d" % (w.num_rows, w.topk))
+    outs = {}
+    for kind in ("int8", "int8_inline"):
+        c = gpu_write(kind, w)
+        oc = oracle_write(kind, w)
+        assert_rows_equal(c, oc, np.arange(oc.num_slots))
+        o, l = run_attention(c, w, out_dtype="fp32")
+        outs[kind] = (o, l)
+        rows = _sample_rows(w.num_rows, 24, 1)
+        ro, rl = oracle_attention(oc, w, rows=rows)
+        ob, lb = run_attention(c, w)          # bf16 output, as benchmarked
+        check(ob[rows], lb[rows], ro, rl, "prefill " + kind)
+        check(o[rows], l[rows], ro, rl, "prefill fp32 " + kind)
+        del c
+    assert np.array_equal(outs["int8"][0], outs["int8_inline"][0])
+    assert np.array_equal(outs["int8"][1], outs["int8_inline"][1])
+
+
+def test_decode_full_size():
+    w = wl.decode(device="cuda")
+    say("decode full: %d rows x topk %d, P %d" % (w.num_rows, w.topk, w.num_splits))
+    c = gpu_write("int8", w)
+    rows = _sample_rows(w.num_rows, 10, 2)
+    toks = needed_tokens(w, rows)
+    rng = np.random.default_rng(5)
+    toks = np.unique(np.concatenate([toks, rng.choice(w.slot_mapping.size, 4096, replace=False)]))
+    oc = oracle_write("int8", w, tokens=toks)
+    assert_rows_equal(c, oc, w.slot_mapping[toks])
+    ro, rl = oracle_attention(oc, w, rows=rows)
+    for P in (w.num_splits, 1):
+        o, l = run_attention(c, w, num_splits=P, decode=True)
+        check(o[rows], l[rows], ro, rl, "decode P%d" % P)
+
+
+@pytest.mark.parametrize("layer", [0, 11])
+def test_e4m3_full_size(layer):
+    w = wl.e4m3_layer(layer, device="cuda")
+    ks, vs = e4m3_scales(w)
+    say("e4m3 layer %d: scales %g %g" % (layer, ks, vs))
+    c = gpu_write("e4m3", w, ks, vs)
+    rows = np.arange(w.num_rows)
+    toks = needed_tokens(w, rows)
+    rng = np.random.default_rng(6)
+    toks = np.unique(np.concatenate([toks, rng.choice(w.slot_mapping.size, 4096, replace=False)]))
+    oc = oracle_write("e4m3", w, ks, vs, tokens=toks)
+    assert_rows_equal(c, oc, w.slot_mapping[toks])
+    ro, rl = oracle_attention(oc, w)
+    for P in (1, 8):
+        o, l = run_attention(c, w, num_splits=P, decode=True)
+        check(o, l, ro, rl, "e4m3 layer %d P%d" % (layer, P))
+
+
+@pytest.mark.parametrize("kind", ["int8", "e4m3", "bf16"])
+def test_e2e_layer_step(kind):
+    """Existing context + an 8192-token chunk written (quantize-on-write) and
+    attended with top-k 1024, then 8 decode steps of one new token each with
+    top-k 2048, in one sequence whose blocks are spread over the 13.75 GiB
+    pool of the cache kind."""
+    tokens = ocache.pool_tokens(wl.E2E_POOL_BYTES, kind, 2, 256, 64)
+    pool_blocks = tokens // 64
+    e = wl.e2e(pool_blocks, device="cuda")
+    say("e2e", kind, "pool blocks", pool_blocks)
+    ks = vs = 1.0
+    if kind == "e4m3":
+        allk = torch.cat([e.ctx_k, e.chunk_k, e.step_k]).abs().max().float().item()
+        allv = torch.cat([e.ctx_v, e.chunk_v, e.step_v]).abs().max().float().item()
+        from oracle import formats as ofmt
+        ks = float(ofmt.e4m3_calibrate_scale(np.array([allk], np.float32)))
+        vs = float(ofmt.e4m3_calibrate_scale(np.array([allv], np.float32)))
+    c = qsakv.Cache(kind, pool_blocks, 64, 2, 256, k_scale=ks, v_scale=vs, zero=False)
+    qsakv.kv_quant_write(c, e.ctx_k, e.ctx_v, dev(e.ctx_slots, torch.int64))
+    qsakv.kv_quant_write(c, e.chunk_k, e.chunk_v, dev(e.chunk_slots, torch.int64))
+    chunk_w = wl.Workload("chunk", 16, 2, 256, 64, pool_blocks, "bf16", "bf16", "bf16",
+                          torch.cat([e.ctx_k, e.chunk_k]), torch.cat([e.ctx_v, e.chunk_v]),
+                          np.concatenate([e.ctx_slots, e.chunk_slots]), e.chunk_q,
+                          np.zeros(e.chunk_q.shape[0], np.int32), e.block_table, e.chunk_topk,
+                          e.sm_scale)
+    o, l = run_attention(c, chunk_w)
+    rows = _sample_rows(chunk_w.num_rows, 12, 3)
+    toks = needed_tokens(chunk_w, rows)
+    step_slots_all = e.step_slots
+    ctx_step = np.concatenate([e.ctx_slots, e.chunk_slots, e.step_slots])
+    k_all = torch.cat([e.ctx_k, e.chunk_k, e.step_k])
+    v_all = torch.cat([e.ctx_v, e.chunk_v, e.step_v])
+    dec_w = wl.Workload("steps", 16, 2, 256, 64, pool_blocks, "bf16", "bf16", "bf16",
+                        k_all, v_all, ctx_step, e.step_q, np.zeros(e.step_q.shape[0], np.int32),
+                        e.block_table, e.step_topk, e.sm_scale, num_splits=8)
+    dtoks = needed_tokens(dec_w, np.arange(dec_w.num_rows))
+    all_toks = np.unique(np.concatenate([toks, dtoks, np.arange(ctx_step.size - 8, ctx_step.size)]))
+    compact = _CompactOracle(kind, dec_w, all_toks, ks, vs)
+    ro, rl = compact.attention(chunk_w, rows)
+    check(o[rows], l[rows], ro, rl, "e2e chunk " + kind)
+    # decode steps: write one token, then attend
+    outs = []
+    for i in range(e.step_k.shape[0]):
+        qsakv.kv_quant_write(c, e.step_k[i:i + 1].contiguous(), e.step_v[i:i + 1].contiguous(),
+                             dev(step_slots_all[i:i + 1], torch.int64))
+        one = wl.Workload("step", 16, 2, 256, 64, pool_blocks, "bf16", "bf16", "bf16",
+                          k_all, v_all, ctx_step, e.step_q[i:i + 1], np.zeros(1, np.int32),
+                          e.block_table, e.step_topk[i:i + 1], e.sm_scale, num_splits=8)
+        outs.append(run_attention(c, one, num_splits=8, decode=True))
+    ro, rl = compact.attention(dec_w, np.arange(dec_w.num_rows))
+    check(np.concatenate([x[0] for x in outs]), np.concatenate([x[1] for x in outs]), ro, rl,
+          "e2e decode " + kind)
+    # the written bytes of every checked token
+    got = _rows_at(c, compact.slots)
+    np.testing.assert_array_equal(got[0], compact.oc.k)
+    np.testing.assert_array_equal(got[1], compact.oc.v)
+    if got[2] is not None:
+        np.testing.assert_array_equal(got[2].view(np.uint32), compact.oc.kv_scale.view(np.uint32))
+    del c
+    torch.cuda.empty_cache()
+
+
+def _rows_at(c, slots):
+    from parity_util import gpu_rows
+    return gpu_rows(c, slots)
+
+
+class _CompactOracle:
+    """Oracle cache holding only the listed tokens, stored densely; attention
+    maps each row's slots into it."""
+
+    def __init__(self, kind, w, toks, ks, vs):
+        self.slots = w.slot_mapping[toks]
+        order = np.argsort(self.slots)
+        self.slots = self.slots[order]
+        toks = toks[order]
+        n = toks.size
+        self.oc = ocache.OracleCache(kind, n, 1, 2, 256, ks if kind == "e4m3" else None,
+                                     vs if kind == "e4m3" else None)
+        ti = torch.as_tensor(toks).to(w.k_src.device)
+        self.oc.write(wl.to_numpy_src(w.k_src[ti]), wl.to_numpy_src(w.v_src[ti]), "bf16",
+                      np.arange(n))
+
+    def attention(self, w, rows):
+        from oracle import attention as oatt
+        qf = oatt.query_to_f64(wl.to_numpy_src(w.q)[rows], w.q_dtype)
+        outs, lses = [], []
+        for i, r in enumerate(rows):
+            slots = oatt.resolve_slots(w.block_table[w.row_seq[r]], w.topk_idx[r], w.block_size)
+            j = np.searchsorted(self.slots, slots)
+            assert np.all(self.slots[j] == slots)
+            o, l = oatt.attend(qf[i], self.oc.dequant(j, "k"), self.oc.dequant(j, "v"), w.sm_scale)
+            outs.append(o)
+            lses.append(l)
+        return np.stack(outs), np.stack(lses)

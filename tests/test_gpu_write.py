@@ -1,0 +1,140 @@
+"""GPU parity of quantize-on-write (kv_quant_write): cache bytes and scales
+must equal the oracle's bit for bit."""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import formats as ofmt
+from quantized_kv_top_amd import qsakv
+from quantized_kv_top_amd import workloads as wl
+
+from parity_util import assert_rows_equal, dev, e4m3_scales, gpu_write, oracle_write, say
+
+pytestmark = pytest.mark.gpu
+
+KINDS = ["int8", "int8_inline", "e4m3", "bf16"]
+
+
+def _scales(kind, w):
+    return e4m3_scales(w) if kind == "e4m3" else (None, None)
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_write_tiny(kind):
+    w = wl.tiny()
+    ks, vs = _scales(kind, w)
+    say("write tiny", kind, ks, vs)
+    c = gpu_write(kind, w, ks or 1.0, vs or 1.0)
+    oc = oracle_write(kind, w, ks, vs)
+    assert_rows_equal(c, oc, np.arange(oc.num_slots))
+
+
+def _special_rows(D, H, rng):
+    """Rows that stress the quantizers: zero, one-hot, constant, tiny
+    (subnormal scale), huge, near-ties, ordinary."""
+    rows = []
+    rows.append(np.zeros(D))
+    oh = np.zeros(D)
+    oh[5] = -3.25
+    rows.append(oh)
+    rows.append(np.full(D, 2.5))
+    rows.append(rng.standard_normal(D) * 1e-38)            # scale underflows
+    rows.append(rng.standard_normal(D) * 1e-41)            # subnormal sources
+    rows.append(rng.standard_normal(D) * 1e30)
+    a = np.float32(37.0)
+    s = np.float32(a / np.float32(127))
+    k = rng.integers(-126, 126, D)
+    ties = ((k + 0.5) * np.float64(s)).astype(np.float32)
+    ties[0] = a
+    rows.append(ties)
+    rows.append(np.nextafter(ties, np.float32(np.inf)))
+    while len(rows) % H:
+        rows.append(rng.standard_normal(D))
+    return np.stack(rows).astype(np.float32)
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("src", ["fp32", "bf16", "fp16"])
+def test_write_dtypes_and_special_rows(kind, D, src):
+    rng = np.random.default_rng(zlib.crc32((kind + str(D) + src).encode()))
+    H, BS, NB = 2, 16, 64
+    special = _special_rows(D, H, rng)
+    T = 300
+    x = (rng.standard_normal((T, H, D)) * np.exp2(rng.uniform(-8, 8, (T, H, 1)))).astype(np.float32)
+    sp = special.reshape(-1, H, D)
+    x[:sp.shape[0]] = sp
+    y = np.roll(x, 7, axis=0)
+    tdt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[src]
+    kt = torch.from_numpy(x).to(tdt)
+    vt = torch.from_numpy(y).to(tdt)
+    if src == "fp16":       # keep fp16 sources finite
+        kt = torch.nan_to_num(kt, posinf=60000.0, neginf=-60000.0)
+        vt = torch.nan_to_num(vt, posinf=60000.0, neginf=-60000.0)
+    slots = rng.permutation(NB * BS)[:T].astype(np.int64)
+    slots[::17] = -1                                   # skipped tokens
+    slots[5] = NB * BS + 3                             # out of range: skipped
+    w = wl.Workload("t", 2 * H, H, D, BS, NB, "bf16", "fp32", src, kt, vt, slots,
+                    torch.zeros(1, 2 * H, D, dtype=torch.bfloat16), np.zeros(1, np.int32),
+                    np.zeros((1, 1), np.int32), np.zeros((1, 1), np.int32), 0.1)
+    ks, vs = (0.0171247218, 0.0841238871) if kind == "e4m3" else (None, None)
+    say("write", kind, D, src)
+    c = gpu_write(kind, w, ks or 1.0, vs or 1.0)
+    good = (slots >= 0) & (slots < NB * BS)
+    w.slot_mapping = np.where(good, slots, -1)
+    oc = oracle_write(kind, w, ks, vs)
+    assert_rows_equal(c, oc, np.arange(NB * BS))
+
+
+def _sweep_values():
+    exps = np.arange(256, dtype=np.uint32)
+    top = np.arange(64, dtype=np.uint32) << np.uint32(17)
+    low = np.array([0, 1, 0xFFFF, 0x10000, 0x10001, 0x1FFFF], dtype=np.uint32)
+    u = (exps[:, None, None] << np.uint32(23)) | top[None, :, None] | low[None, None, :]
+    u = u.ravel()
+    u = np.concatenate([u, u | np.uint32(0x80000000)])
+    return u.view(np.float32)
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.0171247218, 3.0])
+def test_e4m3_encoder_bit_sweep(scale):
+    """Every fp32 sign/exponent with the top 6 mantissa bits and rounding /
+    sticky patterns below them (196,608 values, NaN and inf included) through
+    kv_quant_write; finite results must equal the oracle's codes, NaN
+    sources must give a NaN code."""
+    vals = _sweep_values()
+    D, H = 256, 1
+    T = vals.size // D
+    x = vals[:T * D].reshape(T, H, D)
+    kt = torch.from_numpy(x.copy())
+    slots = np.arange(T, dtype=np.int64)
+    BS = 64
+    NB = -(-T // BS)
+    w = wl.Workload("sweep", 1, 1, D, BS, NB, "bf16", "fp32", "fp32", kt, kt, slots,
+                    torch.zeros(1, 1, D, dtype=torch.bfloat16), np.zeros(1, np.int32),
+                    np.zeros((1, 1), np.int32), np.zeros((1, 1), np.int32), 0.1)
+    say("e4m3 sweep scale", scale, "values", x.size)
+    c = gpu_write("e4m3", w, scale, scale)
+    got = c.k.view(NB * BS, H, D)[:T].cpu().numpy().ravel()
+    want = ofmt.e4m3_quantize(x.ravel(), np.float32(scale))
+    nan = np.isnan(x.ravel())
+    np.testing.assert_array_equal(got[~nan], want[~nan])
+    assert np.all(got[nan] & 0x7F == 0x7F)
+
+
+def test_write_is_deterministic_and_launch_independent():
+    w = wl.prefill(num_rows=4, topk=64, ctx=4096, pool_blocks=80)
+    a = gpu_write("int8", w)
+    b = gpu_write("int8", w)
+    assert torch.equal(a.k, b.k) and torch.equal(a.v, b.v) and torch.equal(a.kv_scale, b.kv_scale)
+    # writing the tokens in two calls of different sizes gives the same cache
+    c = qsakv.Cache("int8", w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
+    sm = dev(w.slot_mapping, torch.int64)
+    ks, vs = w.k_src.cuda(), w.v_src.cuda()
+    qsakv.kv_quant_write(c, ks[:1000].contiguous(), vs[:1000].contiguous(), sm[:1000])
+    qsakv.kv_quant_write(c, ks[1000:].contiguous(), vs[1000:].contiguous(), sm[1000:])
+    torch.cuda.synchronize()
+    assert torch.equal(a.k, c.k) and torch.equal(a.kv_scale, c.kv_scale)
