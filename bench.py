@@ -1,0 +1,371 @@
+"""Benchmark of the top-k sparse-attention hot path on one MI355X.
+
+Default (the default line): the prefill workload -- 2048 query rows x top-k
+1024 over a 32K-token paged int8 cache (Hq 16 / Hkv 2, D 256, BS 64, fp32
+scales in the aligned side tensor), one ``qsa_sparse_attn_prefill`` call per
+step, rotating over independent layer caches (each with its own top-k lists)
+so that more than twice the 256 MB last-level cache passes between two
+visits of the same cache.  Prints ONE JSON line.
+
+Other workloads (``--config``) print their own line for the record:
+decode (8 x 128K, 40 rows, top-k 2048, split-K 8), e4m3 (12 layers, 4 rows,
+top-k 2051, split-K 8 or 1), e2e (chunk write + prefill + 8 decode steps),
+write (quantize-on-write throughput).
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from quantized_kv_top_amd import qsakv                       # noqa: E402
+from quantized_kv_top_amd import workloads as wl              # noqa: E402
+
+METRIC = "top-k sparse-attn query rows/s + gathered-KV HBM GB/s (% of peak), int8/E4M3"
+HBM_PEAK_GBPS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "quantized_kv_top_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def gathered_bytes_per_row(kind, topk, hkv, d):
+    """Algorithmic gathered-KV bytes per query row: every listed token's K and
+    V row of every KV head, plus its int8 scales (4 B each)."""
+    per = {"int8": 2 * (d + 4), "int8_inline": 2 * (d + 4), "e4m3": 2 * d, "bf16": 4 * d}[kind]
+    return topk * hkv * per
+
+
+def traffic_from_profile(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get("%s|%s" % (kernel, workload))
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != source_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+class Timer:
+    """hipEvent pairs around every step on the stream the kernels run on."""
+
+    def __init__(self, stream):
+        self.stream = stream
+        self.pairs = []
+
+    def step(self, fn):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record(self.stream)
+        fn()
+        e.record(self.stream)
+        self.pairs.append((s, e))
+
+    def ms(self):
+        torch.cuda.synchronize()
+        return [s.elapsed_time(e) for s, e in self.pairs]
+
+
+def timed_loop(fn, steps, warmup, stream):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    t = Timer(stream)
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        t.step(lambda: fn(warmup + i))
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = t.ms()
+    return start.elapsed_time(end), per, wall
+
+
+# ---------------------------------------------------------------------------
+# prefill (default)
+# ---------------------------------------------------------------------------
+
+class PrefillLayer:
+    def __init__(self, kind, seed, rows, topk):
+        w = wl.prefill(device="cuda", seed=seed, num_rows=rows, topk=topk)
+        self.w = w
+        self.c = qsakv.Cache(kind, w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
+        qsakv.kv_quant_write(self.c, w.k_src, w.v_src,
+                             torch.from_numpy(w.slot_mapping).cuda())
+        self.q = w.q
+        self.rs = torch.from_numpy(w.row_seq).cuda()
+        self.bt = torch.from_numpy(w.block_table).cuda()
+        self.idx = torch.from_numpy(w.topk_idx).cuda()
+        self.out = torch.empty(w.q.shape, dtype=torch.bfloat16, device="cuda")
+        self.lse = torch.empty(w.q.shape[:2], dtype=torch.float32, device="cuda")
+        w.k_src = w.v_src = None      # free the sources
+
+    def __call__(self, stream):
+        w = self.w
+        qsakv.qsa_sparse_attn_prefill(self.c, self.q, self.rs, self.bt, self.idx, w.sm_scale,
+                                      self.out, lse=self.lse, stream=stream)
+
+
+def cpu_baseline_prefill(seed, budget_s, rows_cap):
+    """The oracle, as it stands, on the first rows of one prefill layer."""
+    from threadpoolctl import threadpool_info
+    from oracle import attention as oatt
+    from oracle import cache as ocache
+
+    w = wl.prefill(device="cpu", seed=seed)
+    oc = ocache.OracleCache("int8", w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
+    t0 = time.perf_counter()
+    oc.write(wl.to_numpy_src(w.k_src), wl.to_numpy_src(w.v_src), "bf16", w.slot_mapping)
+    write_s = time.perf_counter() - t0
+    qn = wl.to_numpy_src(w.q)
+    done = 0
+    t0 = time.perf_counter()
+    while done < rows_cap and time.perf_counter() - t0 < budget_s:
+        oatt.sparse_attention(oc, qn, "bf16", w.row_seq, w.block_table, w.topk_idx,
+                              w.sm_scale, rows=[done % w.num_rows])
+        done += 1
+    el = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": done / el, "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": "%d prefill rows (rows 0.. of %d, cycled; top-k %d, fp64 numpy) in "
+                      "%.1f s; oracle quantize-on-write of all %d tokens took %.1f s"
+                      % (done, w.num_rows, w.topk, el, w.slot_mapping.size, write_s)}
+
+
+def bench_prefill(args):
+    stream = torch.cuda.current_stream()
+    rows, topk = 2048, 1024
+    L = args.layers or 16
+    res = {}
+    for kind in ("int8", "int8_inline"):
+        log("building %d %s prefill layers" % (L, kind))
+        layers = [PrefillLayer(kind, 100 + i, rows, topk) for i in range(L)]
+        torch.cuda.synchronize()
+        total_ms, per, wall = timed_loop(lambda i: layers[i % L](stream), args.steps,
+                                         args.warmup, stream)
+        res[kind] = (total_ms, per, wall)
+        log("%s: %.3f ms/step (events), per-step median %.3f ms" % (
+            kind, total_ms / args.steps, float(np.median(per))))
+        del layers
+        torch.cuda.empty_cache()
+    total_ms, per, wall = res["int8"]
+    ms = total_ms / args.steps
+    value = rows * args.steps / (total_ms / 1e3)
+    bytes_launch = rows * gathered_bytes_per_row("int8", topk, 2, 256)
+    kern_ms = float(np.mean(per))
+    achieved = bytes_launch / (kern_ms / 1e3) / 1e9
+    traffic = traffic_from_profile("qsa_attn_kernel<int8,256>", "prefill")
+    inl_ms = res["int8_inline"][0] / args.steps
+    line = {
+        "metric": METRIC, "value": value, "unit": "rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8", "data": "synthetic",
+        "config": {"workload": "prefill: 2048 query rows x top-k 1024 over a 32768-token paged "
+                               "int8 cache (aligned side-tensor scales), Hq 16 / Hkv 2, D 256, "
+                               "block 64, bf16 Q/out; %d independent layer caches rotated" % L,
+                   "rows": rows, "topk": topk, "num_q_heads": 16, "num_kv_heads": 2,
+                   "head_dim": 256, "block_size": 64, "context": 32768, "layers_rotated": L,
+                   "gathered_kv_bytes_per_step": bytes_launch,
+                   "gathered_kv_GBps": achieved,
+                   "inline260_ms_per_step": inl_ms,
+                   "inline260_over_aligned": inl_ms / ms},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "kernel": "qsa_attn_kernel<int8,256>",
+                     "kernel_ms": kern_ms},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host")
+        line["cpu_baseline"] = cpu_baseline_prefill(100, args.cpu_budget, 1 << 30)
+    return line
+
+
+# ---------------------------------------------------------------------------
+# decode / e4m3 (small launches: timed as captured graphs of L calls)
+# ---------------------------------------------------------------------------
+
+class DecodeLayer:
+    def __init__(self, w, kind, ks=1.0, vs=1.0, splits=8):
+        self.w = w
+        self.splits = splits
+        self.c = qsakv.Cache(kind, w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim,
+                             k_scale=ks, v_scale=vs, zero=False)
+        qsakv.kv_quant_write(self.c, w.k_src, w.v_src, torch.from_numpy(w.slot_mapping).cuda())
+        self.q = w.q.contiguous()
+        self.rs = torch.from_numpy(w.row_seq).cuda()
+        self.bt = torch.from_numpy(w.block_table).cuda()
+        self.idx = torch.from_numpy(w.topk_idx).cuda()
+        R, Hq, D = w.q.shape
+        odt = torch.float16 if w.out_dtype == "fp16" else torch.bfloat16
+        self.out = torch.empty((R, Hq, D), dtype=odt, device="cuda")
+        self.lse = torch.empty((R, Hq), dtype=torch.float32, device="cuda")
+        nb = qsakv.qsa_decode_workspace_bytes(R, Hq, D, splits)
+        self.ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
+        w.k_src = w.v_src = None
+
+    def __call__(self, stream):
+        w = self.w
+        qsakv.qsa_sparse_attn_decode(self.c, self.q, self.rs, self.bt, self.idx, w.sm_scale,
+                                     self.out, self.splits, self.ws, lse=self.lse, stream=stream)
+
+
+def graph_loop(layers, steps, warmup, reps):
+    """Capture one pass over all layers into a graph; time ``steps`` replays."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(2):
+            for lay in layers:
+                lay(s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(reps):
+            for lay in layers:
+                lay(s)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    total, per, wall = timed_loop(lambda i: g.replay(), steps, 0, st)
+    return total, per
+
+
+def bench_decode(args):
+    L = args.layers or 8
+    log("building %d decode layers (8 x 128K tokens each)" % L)
+    layers = [DecodeLayer(wl.decode(device="cuda", seed=200 + i), "int8") for i in range(L)]
+    torch.cuda.synchronize()
+    total, per = graph_loop(layers, args.steps, args.warmup, 1)
+    calls = args.steps * L
+    ms_call = total / calls
+    w = layers[0].w
+    rows = w.num_rows
+    b = rows * gathered_bytes_per_row("int8", w.topk, 2, 256)
+    return {"metric": METRIC, "value": rows / (ms_call / 1e3), "unit": "rows/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_call,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+            "data": "synthetic",
+            "config": {"workload": "decode: 8 seqs x 128K ctx, 5 rows each (40), top-k 2048 "
+                                   "(70%% recent window), split-K 8 + merge, int8 side scales; "
+                                   "%d layers rotated, graph-captured" % L,
+                       "gathered_kv_bytes_per_call": b,
+                       "gathered_kv_GBps": b / (ms_call / 1e3) / 1e9,
+                       "hbm_frac": b / (ms_call / 1e3) / 1e9 / HBM_PEAK_GBPS}}
+
+
+def bench_e4m3(args):
+    L = 12
+    sets = args.layers or 4        # independent caches per layer position
+    splits = args.splits
+    log("building %d x %d E4M3 layers" % (L, sets))
+    layers = []
+    for s in range(sets):
+        for layer in range(L):
+            w = wl.e4m3_layer(layer, device="cuda", seed=4 + 1000 * s)
+            ks = float(np.float32(w.k_src.abs().max().float().item()) / np.float32(448))
+            vs = float(np.float32(w.v_src.abs().max().float().item()) / np.float32(448))
+            layers.append(DecodeLayer(w, "e4m3", ks, vs, splits))
+    torch.cuda.synchronize()
+    total, per = graph_loop(layers, args.steps, args.warmup, 1)
+    ms_step = total / args.steps / sets          # one 12-layer step
+    w = layers[0].w
+    b = L * w.num_rows * gathered_bytes_per_row("e4m3", w.topk, 4, 128)
+    return {"metric": METRIC, "value": L * w.num_rows / (ms_step / 1e3),
+            "unit": "layer-rows/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "e4m3", "data": "synthetic",
+            "config": {"workload": "e4m3: 12 layers x 4 rows, top-k 2051, Hq 32 / Hkv 4, D 128, "
+                                   "split-K %d; %d independent 12-layer sets rotated, "
+                                   "graph-captured" % (splits, sets),
+                       "gathered_kv_bytes_per_step": b,
+                       "gathered_kv_GBps": b / (ms_step / 1e3) / 1e9,
+                       "hbm_frac": b / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBPS}}
+
+
+def bench_write(args):
+    stream = torch.cuda.current_stream()
+    w = wl.decode(device="cuda", seed=300, num_seqs=2)
+    c = qsakv.Cache("int8", w.num_blocks, w.block_size, 2, 256, zero=False)
+    sm = torch.from_numpy(w.slot_mapping).cuda()
+    total, per, wall = timed_loop(lambda i: qsakv.kv_quant_write(c, w.k_src, w.v_src, sm,
+                                                                 stream=stream),
+                                  args.steps, args.warmup, stream)
+    T = w.slot_mapping.size
+    ms = total / args.steps
+    b = T * 2 * 2 * (2 * 256 + 256 + 4)
+    return {"metric": "quantize-on-write tokens/s", "value": T / (ms / 1e3), "unit": "tokens/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+            "data": "synthetic",
+            "config": {"workload": "kv_quant_write int8: %d tokens, Hkv 2, D 256, bf16 src" % T,
+                       "bytes_per_call": b, "GBps": b / (ms / 1e3) / 1e9}}
+
+
+def bench_copy(args):
+    """A plain 1 GiB device copy: the known-size kernel that calibrates the
+    FETCH_SIZE / WRITE_SIZE counters."""
+    x = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(args.steps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    return {"metric": "copy", "value": 1 << 30, "unit": "bytes", "n_gpus": 1}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="prefill",
+                    choices=["prefill", "decode", "e4m3", "write", "copy"])
+    ap.add_argument("--layers", type=int, default=0)
+    ap.add_argument("--splits", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the per-GPU share is the single-GPU workload); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    qsakv.lib()
+    fn = {"prefill": bench_prefill, "decode": bench_decode, "e4m3": bench_e4m3,
+          "write": bench_write, "copy": bench_copy}[args.config]
+    print(json.dumps(fn(args)), flush=True)
+
+
+if __name__ == "__main__":
+    main()
