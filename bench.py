@@ -180,7 +180,7 @@ def bench_prefill(args):
     bytes_launch = rows * gathered_bytes_per_row("int8", topk, 2, 256)
     kern_ms = float(np.mean(per))
     achieved = bytes_launch / (kern_ms / 1e3) / 1e9
-    traffic = traffic_from_profile("qsa_attn_kernel<int8,256>", "prefill")
+    traffic = traffic_from_profile("qsa_attn16_kernel<int8,256>", "prefill")
     inl_ms = res["int8_inline"][0] / args.steps
     line = {
         "metric": METRIC, "value": value, "unit": "rows/s", "n_gpus": 1,
@@ -198,7 +198,7 @@ def bench_prefill(args):
                    "inline260_over_aligned": inl_ms / ms},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel": "qsa_attn_kernel<int8,256>",
+                     "kernel": "qsa_attn16_kernel<int8,256>",
                      "kernel_ms": kern_ms},
     }
     if not args.no_cpu_baseline:
@@ -227,7 +227,7 @@ class DecodeLayer:
         self.out = torch.empty((R, Hq, D), dtype=odt, device="cuda")
         self.lse = torch.empty((R, Hq), dtype=torch.float32, device="cuda")
         nb = qsakv.qsa_decode_workspace_bytes(R, Hq, D, splits)
-        self.ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
+        self.ws = torch.zeros(max(nb, 256), dtype=torch.uint8, device="cuda")
         w.k_src = w.v_src = None
 
     def __call__(self, stream):

@@ -208,7 +208,9 @@ QSAKV_API size_t qsa_decode_workspace_bytes(int32_t num_rows, int32_t num_q_head
  *   num_splits      1..64
  *   workspace       device, >= qsa_decode_workspace_bytes(...), 256-B
  *                   aligned; may be NULL when num_splits == 1.  Its contents
- *                   on entry are ignored and on exit unspecified.
+ *                   on entry are ignored and on exit unspecified; calls that
+ *                   share a workspace must not overlap in time.
+ * Two kernel launches: the partitions, then the merge.
  */
 QSAKV_API qkv_status qsa_sparse_attn_decode(const qkv_cache *cache, const qsa_args *args,
                                   int32_t num_splits, void *workspace, size_t workspace_bytes,

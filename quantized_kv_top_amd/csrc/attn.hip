@@ -12,23 +12,36 @@
 //
 // Work decomposition
 //   One workgroup (4 waves) per (row, KV head, split partition).  The
-//   partition's list positions are cut into super-tiles of 64 positions,
-//   dealt round-robin to the waves; each lane resolves one position to a
-//   slot (index -> block table -> slot).  A super-tile is two 32-token
-//   tiles; the K/V rows of the next tile are in flight (in registers) while
-//   the current one is computed.
+//   workgroup first resolves the partition's positions to slots (index ->
+//   block table -> slot) into LDS, then its waves take the partition's
+//   tiles of TT tokens round-robin, keeping kDepth tiles of gathered rows in
+//   registers: kDepth - 1 in flight while one is computed.  Waves merge in
+//   LDS in a fixed order (bitwise reproducible).  With several partitions,
+//   each writes an unnormalized partial and a second, small launch merges
+//   them (log-sum-exp).
 //
-// Per 32-token tile, in MFMA 16x16x32 terms (GQA heads on the N side):
+// Per tile, in MFMA 16x16 terms with the row's G <= 16 query heads on N:
 //   S^T[t][h] = K[t][:] . Q[h][:]          A = K rows (M = 16 tokens), B = Q^T
 //   online softmax over the tile (log2 domain, running max per head)
 //   O^T[d][h] += V^T[d][t] . W[t][h]       A = V^T (M = 16 d's), B = W
-// so the row's G <= 16 query heads share every gathered K/V tile.  The int8
-// and E4M3 codes become exact fp16 operands in registers; Q is rounded to
-// fp16 after an exact power-of-two prescale; bf16 caches run bf16 MFMA.
-// The int8 per-token K scale multiplies the logit after the dot product; the
-// per-token V scale is folded into the softmax weight W = p * s_v / sigma,
-// with sigma the running maximum V scale of the wave (kept exact by
-// rescaling the accumulator by a power-free ratio when it grows).
+// so the G query heads share every gathered K/V tile.  The QK^T output of a
+// 16-token block gives each lane 4 tokens of one head, which is exactly the
+// B operand of a K = 16 MFMA (TT = 16) or half of a K = 32 one (TT = 32).
+//
+// Exact operands.  E4M3 codes become fp16 through gfx950's OCP-FP8 convert.
+// An int8 code q becomes the fp16 value 1152 + q (0x64 in the high byte and
+// q + 128 in the low byte -- exact, one byte permute per pair); the constant
+// 1152 is removed after the MFMA: from each logit as 1152 * sum_d q'_d, and
+// from the output as 1152 * sum_t W_t, both sums of exactly what entered the
+// MFMA.  Queries are rounded to fp16 after an exact power-of-two prescale;
+// bf16 caches run bf16 MFMA directly.
+//
+// Scales.  The int8 per-token K scale multiplies the logit after the dot
+// product; the per-token V scale enters the softmax weight
+// W = p * s_v / sigma (sigma a running reference V scale).  The running max
+// m and sigma are only moved when a tile exceeds them by 2^8 (m) or 16x
+// (sigma): weights stay below 2^12, far inside fp16, and the accumulator is
+// rescaled only on those rare moves.
 #include "qsakv_device.h"
 #include "qsakv_internal.h"
 
@@ -36,57 +49,66 @@ namespace qsakv {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kSuper = 64;   // list positions per super-tile (one per lane)
+constexpr int kChunk = 1024;          // list positions resolved per LDS batch
 constexpr float kNegInf = -__builtin_inff();
+constexpr float kMaxSlack = 8.f;      // log2 units the running max may lag behind
+constexpr float kSigSlack = 16.f;     // factor sigma may lag behind a tile's V scale
+constexpr float kI8Bias = 1152.f;     // fp16(0x64XX) = 1024 + XX, XX = q + 128
 
-template <int KIND, int D>
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+template <int KIND, int D, int TT>
 struct Geo {
   static constexpr bool kOneByte = KIND != kBF16;
+  static constexpr bool kInt = KIND == kInt8 || KIND == kInt8Inline;
   static constexpr int kDataBytes = kOneByte ? D : 2 * D;              // K or V row payload
   static constexpr int kRowBytes = KIND == kInt8Inline ? D + 4 : kDataBytes;
   static constexpr int kKChunks = kDataBytes / 64;                      // 16-B chunks / lane / token
   static constexpr int kVBytes = kDataBytes / 16;                       // bytes / lane / token
   static constexpr int kVWords = kVBytes / 4;
   static constexpr int kQK = D / 32;                                    // MFMAs per 16 tokens
-  static constexpr int kPV = D / 16;                                    // MFMAs per tile
+  static constexpr int kPV = D / 16;                                    // PV MFMAs per tile
   static constexpr int kOut = D / 4;                                    // outputs per lane
+  static constexpr int kBlk = TT / 16;                                  // 16-token blocks
+  static constexpr int kTok = TT / 4;                                   // V tokens per lane
+  // tiles held in registers per wave: three where they fit next to the
+  // accumulators, else two
+  static constexpr int kDepth = (TT == 32 && kOneByte && D == 256) ? 3 : 2;
 };
 
-// Raw gathered data of one 32-token tile, as held by one lane.
-template <int KIND, int D>
+// Raw gathered data of one tile, as held by one lane.
+template <int KIND, int D, int TT>
 struct TileRaw {
-  using G = Geo<KIND, D>;
-  u32x4 k[2][G::kKChunks];          // tokens ln16 and 16 + ln16
-  uint32_t v[8][G::kVWords];        // tokens tok(grp, e), e = 0..7
-  float sk[8], sv[8];               // int8 scales of tokens tok(grp, e)
+  using G = Geo<KIND, D, TT>;
+  u32x4 k[G::kBlk][G::kKChunks];    // tokens 16 b + ln16
+  uint32_t v[G::kTok][G::kVWords];  // tokens tok(grp, e)
+  float sk[G::kTok], sv[G::kTok];   // int8 scales of tokens tok(grp, e)
   uint32_t valid;                   // bit e: token tok(grp, e) is attended
 };
-
-// Token (0..31 within the tile) held in k-slot e of lane group grp: the
-// order in which the QK^T output of the two 16-token halves lands in a lane.
-__device__ __forceinline__ int tok_of(int grp, int e) {
-  return e < 4 ? 4 * grp + e : 16 + 4 * grp + (e - 4);
-}
 
 template <typename T>
 __device__ __forceinline__ T ld(const uint8_t* p) { return *reinterpret_cast<const T*>(p); }
 
-// Issue the loads of one tile.  `slot` is this lane's resolved slot of list
-// position (super-tile base + lane); `half` selects positions 0..31 or 32..63.
-template <int KIND, int D>
-__device__ __forceinline__ void issue_tile(TileRaw<KIND, D>& t, const AttnParams& p, int g,
-                                           int slot, int half) {
-  using G = Geo<KIND, D>;
+// Issue the loads of one tile whose resolved slots (-1 = padding) are
+// ts[0..TT) in LDS.  Lane (ln16, grp) gathers the K rows of tokens 16 b +
+// ln16 (16 bytes per 64-byte chunk) and the V rows and scales of tokens
+// 4 grp .. 4 grp + 3 (+16): the k-slot order in which the QK^T output of a
+// 16-token block lands in a lane.
+template <int KIND, int D, int TT>
+__device__ __forceinline__ void issue_tile(TileRaw<KIND, D, TT>& t, const AttnParams& p, int g,
+                                           const int* ts) {
+  using G = Geo<KIND, D, TT>;
   const int lane = lane_id(), ln16 = lane & 15, grp = lane >> 4;
   const int hkv = p.num_kv_heads;
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int s = __shfl(slot, half * 32 + b * 16 + ln16);
+  for (int b = 0; b < G::kBlk; ++b) {
+    const int s = ts[b * 16 + ln16];
     const int64_t row = ((int64_t)(s < 0 ? 0 : s) * hkv + g) * G::kRowBytes;
     const uint8_t* kr = p.k + row + 16 * grp;
 #pragma unroll
     for (int c = 0; c < G::kKChunks; ++c) {
-      if constexpr (KIND == kInt8Inline) {
+      if constexpr (KIND == kInt8Inline) {   // 4-byte aligned rows: dword loads
         const uint32_t* w = reinterpret_cast<const uint32_t*>(kr + 64 * c);
         t.k[b][c] = u32x4{w[0], w[1], w[2], w[3]};
       } else {
@@ -94,14 +116,23 @@ __device__ __forceinline__ void issue_tile(TileRaw<KIND, D>& t, const AttnParams
       }
     }
   }
+  int vs[G::kTok];
+  {
+    const int4 s0 = *reinterpret_cast<const int4*>(ts + 4 * grp);
+    vs[0] = s0.x; vs[1] = s0.y; vs[2] = s0.z; vs[3] = s0.w;
+    if constexpr (G::kTok == 8) {
+      const int4 s1 = *reinterpret_cast<const int4*>(ts + 16 + 4 * grp);
+      vs[4] = s1.x; vs[5] = s1.y; vs[6] = s1.z; vs[7] = s1.w;
+    }
+  }
   uint32_t valid = 0;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int s = __shfl(slot, half * 32 + tok_of(grp, e));
+  for (int e = 0; e < G::kTok; ++e) {
+    const int s = vs[e];
     valid |= (s >= 0 ? 1u : 0u) << e;
     const int64_t rowi = (int64_t)(s < 0 ? 0 : s) * hkv + g;
     const uint8_t* vr = p.v + rowi * G::kRowBytes + ln16 * G::kVBytes;
-    if constexpr (KIND == kInt8Inline) {  // 4-byte aligned rows: dword loads
+    if constexpr (KIND == kInt8Inline) {
       const uint32_t* wv = reinterpret_cast<const uint32_t*>(vr);
 #pragma unroll
       for (int i = 0; i < G::kVWords; ++i) t.v[e][i] = wv[i];
@@ -140,24 +171,47 @@ __device__ __forceinline__ void issue_tile(TileRaw<KIND, D>& t, const AttnParams
 }
 
 struct WaveState {
-  float m;     // running max of the logits (log2 domain), per head
+  float m;     // running max in use (log2 domain), per head
   float l;     // this lane's partial sum of exp2(logit - m)
-  float sig;   // running max V scale (int8 kinds), wave-uniform
+  float sig;   // reference V scale (int8 kinds), wave-uniform
+  float cw;    // this lane's partial sum of the PV weights (int8 bias removal)
 };
 
-template <int KIND, int D>
+template <int KIND>
 using QOp = std::conditional_t<KIND == kBF16, bf16x8, f16x8>;
 
-template <int KIND, int D>
-__device__ __forceinline__ void compute_tile(const TileRaw<KIND, D>& t,
-                                             const QOp<KIND, D> (&q)[Geo<KIND, D>::kQK],
-                                             float kfac, WaveState& st,
-                                             f32x4 (&o)[Geo<KIND, D>::kPV]) {
-  using G = Geo<KIND, D>;
-  // ---- S^T = K Q^T for the two 16-token halves --------------------------
-  f32x4 s[2];
+// Byte lanes of the token pair (x, y) interleaved: tk[0] = (x0 y0 x1 y1),
+// tk[1] = (x2 y2 x3 y3); int8 codes are biased to q + 128 on the way.
+template <int KIND>
+__device__ __forceinline__ void interleave_pair(uint32_t x, uint32_t y, uint32_t (&tk)[2]) {
+  tk[0] = perm(y, x, 0x05010400u);
+  tk[1] = perm(y, x, 0x07030602u);
+  if constexpr (KIND != kE4M3) {
+    tk[0] ^= 0x80808080u;
+    tk[1] ^= 0x80808080u;
+  }
+}
+// The fp16 pair (x_j, y_j) for byte j = bb of the interleaved words.
+template <int KIND>
+__device__ __forceinline__ uint32_t v_pair_f16(const uint32_t (&tk)[2], int bb) {
+  const int half = bb >> 1, hi = bb & 1;
+  if constexpr (KIND == kE4M3)
+    return hi ? e4m3pair_to_f16x2<true>(tk[half]) : e4m3pair_to_f16x2<false>(tk[half]);
+  else
+    return i8pair_to_f16x2(tk[half], hi ? kSelB23 : kSelB01);
+}
+
+template <int KIND, int D, int TT>
+__device__ __forceinline__ void compute_tile(const TileRaw<KIND, D, TT>& t,
+                                             const QOp<KIND> (&q)[Geo<KIND, D, TT>::kQK],
+                                             float kfac, float kbias, WaveState& st,
+                                             f32x4 (&o)[Geo<KIND, D, TT>::kPV]) {
+  using G = Geo<KIND, D, TT>;
+  constexpr int NT = G::kTok;
+  // ---- S^T = K Q^T for the 16-token blocks -------------------------------
+  f32x4 s[G::kBlk];
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
+  for (int b = 0; b < G::kBlk; ++b) {
     s[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < G::kQK; ++i) {
@@ -166,51 +220,76 @@ __device__ __forceinline__ void compute_tile(const TileRaw<KIND, D>& t,
       } else {
         const u32x4& c = t.k[b][i >> 1];
         const uint32_t w0 = c[2 * (i & 1)], w1 = c[2 * (i & 1) + 1];
-        const f16x8 a = (KIND == kE4M3) ? e4m3x8_to_f16(w0, w1) : i8x8_to_f16(w0, w1);
-        s[b] = mfma16(a, q[i], s[b]);
+        u32x4 a;
+        if constexpr (KIND == kE4M3) {
+          a[0] = e4m3pair_to_f16x2<false>(w0);
+          a[1] = e4m3pair_to_f16x2<true>(w0);
+          a[2] = e4m3pair_to_f16x2<false>(w1);
+          a[3] = e4m3pair_to_f16x2<true>(w1);
+        } else {
+          const uint32_t x0 = w0 ^ 0x80808080u, x1 = w1 ^ 0x80808080u;
+          a[0] = i8pair_to_f16x2(x0, kSelB01);
+          a[1] = i8pair_to_f16x2(x0, kSelB23);
+          a[2] = i8pair_to_f16x2(x1, kSelB01);
+          a[3] = i8pair_to_f16x2(x1, kSelB23);
+        }
+        s[b] = mfma16(bitcast<f16x8>(a), q[i], s[b]);
       }
     }
   }
   // ---- online softmax in the log2 domain --------------------------------
-  float y[8];
+  float y[NT];
   float mx = kNegInf;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float raw = e < 4 ? s[0][e] : s[1][e - 4];
+  for (int e = 0; e < NT; ++e) {
+    float raw = s[e >> 2][e & 3];
     float f = kfac;
-    if constexpr (KIND == kInt8 || KIND == kInt8Inline) f *= t.sk[e];
+    if constexpr (G::kInt) {
+      raw -= kbias;
+      f *= t.sk[e];
+    }
     y[e] = ((t.valid >> e) & 1u) ? raw * f : kNegInf;
     mx = fmaxf(mx, y[e]);
   }
   mx = group4_max(mx);
-  const float m_new = fmaxf(st.m, mx);
-  const float m_use = m_new == kNegInf ? 0.f : m_new;
-  const float alpha = __builtin_amdgcn_exp2f(st.m - m_use);
-  float pr[8], psum = 0.f;
+  float alpha = 1.f;
+  if (mx > st.m + kMaxSlack) {           // the running max moves (rare)
+    alpha = __builtin_amdgcn_exp2f(st.m - mx);
+    st.m = mx;
+  }
+  const float m_use = st.m == kNegInf ? 0.f : st.m;
+  float pr[NT], psum = 0.f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
+  for (int e = 0; e < NT; ++e) {
     pr[e] = __builtin_amdgcn_exp2f(y[e] - m_use);
     psum += pr[e];
   }
   st.l = st.l * alpha + psum;
-  st.m = m_new;
 
   float beta = alpha;
-  float w[8];
-  if constexpr (KIND == kInt8 || KIND == kInt8Inline) {
+  float w[NT];
+  if constexpr (G::kInt) {
     float smax = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) smax = fmaxf(smax, ((t.valid >> e) & 1u) ? t.sv[e] : 0.f);
+    for (int e = 0; e < NT; ++e) smax = fmaxf(smax, ((t.valid >> e) & 1u) ? t.sv[e] : 0.f);
     smax = group4_max(smax);
-    const float sig_new = fmaxf(st.sig, smax);
-    const float rs = sig_new > 0.f ? 1.f / sig_new : 0.f;
-    beta = alpha * (st.sig * rs);
-    st.sig = sig_new;
+    if (smax > st.sig * kSigSlack) {     // the reference V scale moves (rare)
+      beta *= st.sig / smax;
+      st.sig = smax;
+    }
+    const float rs = st.sig > 0.f ? 1.f / st.sig : 0.f;
+    float wsum = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) w[e] = pr[e] * (t.sv[e] * rs);
+    for (int e = 0; e < NT; ++e) {
+      // the weight as it enters the MFMA (fp16), so that the bias removed
+      // afterwards is exactly the one the MFMA added
+      w[e] = (float)(_Float16)(pr[e] * (t.sv[e] * rs));
+      wsum += w[e];
+    }
+    st.cw = st.cw * beta + wsum;
   } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) w[e] = pr[e];
+    for (int e = 0; e < NT; ++e) w[e] = pr[e];
   }
   if (__any(beta != 1.f)) {
 #pragma unroll
@@ -218,67 +297,99 @@ __device__ __forceinline__ void compute_tile(const TileRaw<KIND, D>& t,
   }
   // ---- O^T += V^T W -------------------------------------------------------
   if constexpr (KIND == kBF16) {
-    bf16x8 bw;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) bw[e] = (__bf16)w[e];
 #pragma unroll
     for (int c = 0; c < G::kVWords; ++c) {
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
-        u32x4 a;
+        const uint32_t sel = hb ? 0x07060302u : 0x05040100u;
+        if constexpr (TT == 32) {
+          bf16x8 bw;
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-          a[k] = perm(t.v[2 * k + 1][c], t.v[2 * k][c], hb ? 0x07060302u : 0x05040100u);
-        o[2 * c + hb] = mfma16(bitcast<bf16x8>(a), bw, o[2 * c + hb]);
+          for (int e = 0; e < 8; ++e) bw[e] = (__bf16)w[e];
+          u32x4 a;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) a[k] = perm(t.v[2 * k + 1][c], t.v[2 * k][c], sel);
+          o[2 * c + hb] = mfma16(bitcast<bf16x8>(a), bw, o[2 * c + hb]);
+        } else {
+          bf16x4 bw;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) bw[e] = (__bf16)w[e];
+          u32x2 a;
+          a[0] = perm(t.v[1][c], t.v[0][c], sel);
+          a[1] = perm(t.v[3][c], t.v[2][c], sel);
+          o[2 * c + hb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bitcast<bf16x4>(a), bw,
+                                                                     o[2 * c + hb], 0, 0, 0);
+        }
       }
     }
   } else {
-    f16x8 bw;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) bw[e] = (_Float16)w[e];
 #pragma unroll
     for (int c = 0; c < G::kVWords; ++c) {
-      // interleave the byte lanes of token pairs: tk[k][0] = (x0 y0 x1 y1),
-      // tk[k][1] = (x2 y2 x3 y3) for x = token 2k, y = token 2k+1
-      uint32_t tk[4][2];
+      uint32_t tk[NT / 2][2];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        uint32_t x = t.v[2 * k][c], yv = t.v[2 * k + 1][c];
-        if constexpr (KIND != kE4M3) {
-          x ^= 0x80808080u;
-          yv ^= 0x80808080u;
-        }
-        tk[k][0] = perm(yv, x, 0x05010400u);
-        tk[k][1] = perm(yv, x, 0x07030602u);
-      }
+      for (int k = 0; k < NT / 2; ++k) interleave_pair<KIND>(t.v[2 * k][c], t.v[2 * k + 1][c], tk[k]);
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) {
-        const int half = bb >> 1, hi = bb & 1;
-        f16x8 a;
-        if constexpr (KIND == kE4M3) {
+        if constexpr (TT == 32) {
+          f16x8 bw;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) bw[e] = (_Float16)w[e];
           u32x4 r;
 #pragma unroll
-          for (int k = 0; k < 4; ++k)
-            r[k] = hi ? e4m3pair_to_f16x2<true>(tk[k][half])
-                      : e4m3pair_to_f16x2<false>(tk[k][half]);
-          a = bitcast<f16x8>(r);
+          for (int k = 0; k < 4; ++k) r[k] = v_pair_f16<KIND>(tk[k], bb);
+          o[4 * c + bb] = mfma16(bitcast<f16x8>(r), bw, o[4 * c + bb]);
         } else {
-          u32x4 r;
+          f16x4 bw;
 #pragma unroll
-          for (int k = 0; k < 4; ++k) r[k] = i8pair_to_f16x2(tk[k][half], hi ? kSelB23 : kSelB01);
-          a = sub1152(r);
+          for (int e = 0; e < 4; ++e) bw[e] = (_Float16)w[e];
+          u32x2 r;
+          r[0] = v_pair_f16<KIND>(tk[0], bb);
+          r[1] = v_pair_f16<KIND>(tk[1], bb);
+          o[4 * c + bb] = __builtin_amdgcn_mfma_f32_16x16x16f16(bitcast<f16x4>(r), bw,
+                                                                 o[4 * c + bb], 0, 0, 0);
         }
-        o[4 * c + bb] = mfma16(a, bw, o[4 * c + bb]);
       }
     }
   }
 }
 
-template <int KIND, int D>
-__global__ __launch_bounds__(kWaves * kWave) void qsa_attn_kernel(AttnParams p) {
-  using G = Geo<KIND, D>;
+// Store D/4 contiguous floats (a lane's share of one head's output row).
+template <int N>
+__device__ __forceinline__ void store_row(void* out, int out_dtype, int64_t off, const float* v) {
+  if (out_dtype == kDtFP32) {
+    float4* dst = reinterpret_cast<float4*>(static_cast<float*>(out) + off);
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) dst[i] = float4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+  } else {
+    u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + off);
+#pragma unroll
+    for (int i = 0; i < N / 8; ++i) {
+      u32x4 q;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (out_dtype == kDtBF16) {
+          bf16x2 b;
+          b[0] = (__bf16)v[8 * i + 2 * k];
+          b[1] = (__bf16)v[8 * i + 2 * k + 1];
+          q[k] = bitcast<uint32_t>(b);
+        } else {
+          f16x2 h;
+          h[0] = (_Float16)v[8 * i + 2 * k];
+          h[1] = (_Float16)v[8 * i + 2 * k + 1];
+          q[k] = bitcast<uint32_t>(h);
+        }
+      }
+      dst[i] = q;
+    }
+  }
+}
+
+template <int KIND, int D, int TT>
+__device__ __forceinline__ void attn_body(const AttnParams& p) {
+  using G = Geo<KIND, D, TT>;
   __shared__ float s_obuf[G::kOut * kWave];
   __shared__ float s_m[kWaves][16], s_l[kWaves][16], s_sig[kWaves];
+  __shared__ __align__(16) int s_slot[kChunk];
 
   const int lane = lane_id(), ln16 = lane & 15, grp = lane >> 4;
   const int w = threadIdx.x >> 6;
@@ -304,11 +415,45 @@ __global__ __launch_bounds__(kWaves * kWave) void qsa_attn_kernel(AttnParams p) 
   const int32_t* bt_row = p.block_table + (int64_t)(seq_ok ? seq : 0) * p.bt_stride;
   const int bs_mask = (1 << p.log2_bs) - 1;
 
-  // ---- Q operand (B of QK^T) and the logit factor -------------------------
+  // ---- slots of the partition, resolved into LDS a chunk at a time --------
+  // (position -> block table -> slot; -1 for padding and for anything out of
+  // range).  Each thread resolves kChunk / 256 positions.
+  constexpr int kPer = kChunk / (kWaves * kWave);
+  int cpos[kPer];
+  auto chunk_start = [&](int c0) {
+    const int cn = min(kChunk, npos - c0);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = threadIdx.x + u * kWaves * kWave;
+      cpos[u] = i < cn ? idx_row[c0 + i] : -1;
+    }
+  };
+  auto chunk_finish = [&](int c0) {
+    const int cn = min(kChunk, npos - c0);
+    const int rounded = (cn + TT - 1) / TT * TT;
+    int blk[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int pos = cpos[u];
+      const int lb = pos >> p.log2_bs;
+      blk[u] = (pos >= 0 && lb < p.bt_stride) ? bt_row[lb] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = threadIdx.x + u * kWaves * kWave;
+      const int pos = cpos[u];
+      if (i < rounded)
+        s_slot[i] = (blk[u] >= 0 && blk[u] < p.num_blocks) ? (blk[u] << p.log2_bs) + (pos & bs_mask)
+                                                            : -1;
+    }
+  };
+  if (npos > 0) chunk_start(0);     // the index loads start before the query is read
+
+  // ---- Q operand (B of QK^T), the logit factor and the int8 bias term ----
   const bool head_ok = ln16 < p.group;
   const int hq = g * p.group + ln16;
-  QOp<KIND, D> qop[G::kQK];
-  float kfac;
+  QOp<KIND> qop[G::kQK];
+  float kfac, kbias = 0.f;
   {
     const int64_t qoff = ((int64_t)r * p.num_q_heads + (head_ok ? hq : 0)) * D;
     const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + qoff;
@@ -322,92 +467,106 @@ __global__ __launch_bounds__(kWaves * kWave) void qsa_attn_kernel(AttnParams p) 
 #pragma unroll
       for (int i = 0; i < G::kQK; ++i) qop[i] = bitcast<bf16x8>(raw[i]);
       kfac = p.sm_log2e;
-    } else if (p.q_dtype == kDtFP16) {
-#pragma unroll
-      for (int i = 0; i < G::kQK; ++i) qop[i] = bitcast<f16x8>(raw[i]);
-      kfac = p.sm_log2e * p.k_scale;
     } else {
-      // bf16 queries: exact power-of-two prescale so max|q| lands in
-      // [2^14, 2^15), then round to fp16 (exact for every element >= 2^-14
-      // after scaling; smaller ones keep an absolute error <= 2^-25).
-      float amax = 0.f;
+      int e = 0;
+      if (p.q_dtype == kDtFP16) {
 #pragma unroll
-      for (int i = 0; i < G::kQK; ++i)
+        for (int i = 0; i < G::kQK; ++i) qop[i] = bitcast<f16x8>(raw[i]);
+      } else {
+        // bf16 queries: exact power-of-two prescale so max|q| lands in
+        // [2^14, 2^15), then round to fp16 (exact for every element >= 2^-14
+        // after scaling; smaller ones keep an absolute error <= 2^-25).
+        float amax = 0.f;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          amax = fmaxf(amax, fabsf(__uint_as_float(raw[i][k] << 16)));
-          amax = fmaxf(amax, fabsf(__uint_as_float(raw[i][k] & 0xFFFF0000u)));
+        for (int i = 0; i < G::kQK; ++i)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            amax = fmaxf(amax, fabsf(__uint_as_float(raw[i][k] << 16)));
+            amax = fmaxf(amax, fabsf(__uint_as_float(raw[i][k] & 0xFFFF0000u)));
+          }
+        amax = group4_max(amax);
+        int ex = 0;
+        if (amax > 0.f) frexpf(amax, &ex);
+        e = amax > 0.f ? 15 - ex : 0;
+        e = e > 127 ? 127 : (e < -126 ? -126 : e);
+        const float sc = ldexpf(1.f, e);
+#pragma unroll
+        for (int i = 0; i < G::kQK; ++i) {
+          f16x8 h;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            h[2 * k] = (_Float16)(__uint_as_float(raw[i][k] << 16) * sc);
+            h[2 * k + 1] = (_Float16)(__uint_as_float(raw[i][k] & 0xFFFF0000u) * sc);
+          }
+          qop[i] = h;
         }
-      amax = group4_max(amax);
-      int ex = 0;
-      if (amax > 0.f) frexpf(amax, &ex);
-      int e = amax > 0.f ? 15 - ex : 0;
-      e = e > 127 ? 127 : (e < -126 ? -126 : e);
-      const float sc = ldexpf(1.f, e);
-#pragma unroll
-      for (int i = 0; i < G::kQK; ++i) {
-        f16x8 h;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          h[2 * k] = (_Float16)(__uint_as_float(raw[i][k] << 16) * sc);
-          h[2 * k + 1] = (_Float16)(__uint_as_float(raw[i][k] & 0xFFFF0000u) * sc);
-        }
-        qop[i] = h;
       }
       kfac = p.sm_log2e * p.k_scale * ldexpf(1.f, -e);
+      if constexpr (G::kInt) {
+        float qs = 0.f;
+#pragma unroll
+        for (int i = 0; i < G::kQK; ++i)
+#pragma unroll
+          for (int k = 0; k < 8; ++k) qs += (float)qop[i][k];
+        kbias = kI8Bias * group4_sum(qs);
+      }
     }
   }
 
-  // ---- the wave's super-tiles ---------------------------------------------
-  const int nsuper = (npos + kSuper - 1) / kSuper;
-  const int my_n = nsuper > w ? (nsuper - w + kWaves - 1) / kWaves : 0;
-  auto load_pos = [&](int k) -> int {
-    if (k >= my_n) return -1;
-    const int j = (w + kWaves * k) * kSuper + lane;
-    return j < npos ? idx_row[j] : -1;
-  };
-  auto load_blk = [&](int pos) -> int {
-    if (pos < 0) return -1;
-    const int lb = pos >> p.log2_bs;
-    return lb < p.bt_stride ? bt_row[lb] : -1;
-  };
-  auto make_slot = [&](int pos, int blk) -> int {
-    return (blk >= 0 && blk < p.num_blocks) ? (blk << p.log2_bs) + (pos & bs_mask) : -1;
-  };
-
-  WaveState st{kNegInf, 0.f, 0.f};
+  // ---- the wave's tiles -----------------------------------------------------
+  WaveState st{kNegInf, 0.f, 0.f, 0.f};
   f32x4 o[G::kPV];
 #pragma unroll
   for (int j = 0; j < G::kPV; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (my_n > 0) {
-    TileRaw<KIND, D> ta, tb;
-    int pos1 = load_pos(1);
-    int pos0 = load_pos(0);
-    int slot = make_slot(pos0, load_blk(pos0));
-    issue_tile<KIND, D>(ta, p, g, slot, 0);
-    int blk1 = load_blk(pos1);
-    int pos2 = load_pos(2);
-    issue_tile<KIND, D>(tb, p, g, slot, 1);
-    for (int k = 0; k < my_n; ++k) {
-      compute_tile<KIND, D>(ta, qop, kfac, st, o);
-      const bool more = k + 1 < my_n;
-      if (more) {
-        slot = make_slot(pos1, blk1);
-        issue_tile<KIND, D>(ta, p, g, slot, 0);
+  for (int c0 = 0; c0 < npos; c0 += kChunk) {
+    if (c0 > 0) {
+      __syncthreads();               // the previous chunk's slots are consumed
+      chunk_start(c0);
+    }
+    chunk_finish(c0);
+    __syncthreads();
+    const int ntiles = (min(kChunk, npos - c0) + TT - 1) / TT;
+    const int my_n = ntiles > w ? (ntiles - w + kWaves - 1) / kWaves : 0;
+    // tiles w, w + 4, w + 8, ... of the chunk, kDepth of them in registers:
+    // kDepth - 1 in flight while one is computed
+    auto ts = [&](int k) { return s_slot + (w + kWaves * k) * TT; };
+    TileRaw<KIND, D, TT> ta, tb, tc;
+    if (my_n > 0) issue_tile<KIND, D, TT>(ta, p, g, ts(0));
+    if (my_n > 1) issue_tile<KIND, D, TT>(tb, p, g, ts(1));
+    if constexpr (G::kDepth == 3) {
+      if (my_n > 2) issue_tile<KIND, D, TT>(tc, p, g, ts(2));
+      for (int k = 0; k < my_n; k += 3) {
+        compute_tile<KIND, D, TT>(ta, qop, kfac, kbias, st, o);
+        if (k + 3 < my_n) issue_tile<KIND, D, TT>(ta, p, g, ts(k + 3));
+        if (k + 1 < my_n) {
+          compute_tile<KIND, D, TT>(tb, qop, kfac, kbias, st, o);
+          if (k + 4 < my_n) issue_tile<KIND, D, TT>(tb, p, g, ts(k + 4));
+        }
+        if (k + 2 < my_n) {
+          compute_tile<KIND, D, TT>(tc, qop, kfac, kbias, st, o);
+          if (k + 5 < my_n) issue_tile<KIND, D, TT>(tc, p, g, ts(k + 5));
+        }
       }
-      const int blk2 = load_blk(pos2);
-      const int pos3 = load_pos(k + 3);
-      compute_tile<KIND, D>(tb, qop, kfac, st, o);
-      if (more) issue_tile<KIND, D>(tb, p, g, slot, 1);
-      pos1 = pos2;
-      blk1 = blk2;
-      pos2 = pos3;
+    } else {
+      for (int k = 0; k < my_n; k += 2) {
+        compute_tile<KIND, D, TT>(ta, qop, kfac, kbias, st, o);
+        if (k + 2 < my_n) issue_tile<KIND, D, TT>(ta, p, g, ts(k + 2));
+        if (k + 1 < my_n) {
+          compute_tile<KIND, D, TT>(tb, qop, kfac, kbias, st, o);
+          if (k + 3 < my_n) issue_tile<KIND, D, TT>(tb, p, g, ts(k + 3));
+        }
+      }
     }
   }
 
   // ---- merge the waves' partial results -----------------------------------
   const float l_h = group4_sum(st.l);
+  if constexpr (G::kInt) {
+    const float corr = kI8Bias * group4_sum(st.cw);
+#pragma unroll
+    for (int j = 0; j < G::kPV; ++j) o[j] -= corr;
+  }
   if (grp == 0) {
     s_m[w][ln16] = st.m;
     s_l[w][ln16] = l_h;
@@ -425,7 +584,7 @@ __global__ __launch_bounds__(kWaves * kWave) void qsa_attn_kernel(AttnParams p) 
     L += f * s_l[i][ln16];
     if (i == w) myf = f;
   }
-  if constexpr (KIND == kInt8 || KIND == kInt8Inline) myf *= st.sig;
+  if constexpr (G::kInt) myf *= st.sig;
   for (int i = 0; i < kWaves - 1; ++i) {
     if (w == i) {
 #pragma unroll
@@ -439,7 +598,7 @@ __global__ __launch_bounds__(kWaves * kWave) void qsa_attn_kernel(AttnParams p) 
     }
     __syncthreads();
   }
-  if (w != kWaves - 1) return;
+  if (w != kWaves - 1 || !head_ok) return;
 #pragma unroll
   for (int j = 0; j < G::kPV; ++j)
 #pragma unroll
@@ -449,7 +608,6 @@ __global__ __launch_bounds__(kWaves * kWave) void qsa_attn_kernel(AttnParams p) 
   // D/4 contiguous outputs starting at (D/4) * grp.
   const int64_t orow = (int64_t)r * p.num_q_heads + hq;
   if (p.num_splits == 1) {
-    if (!head_ok) return;
     const bool any = L > 0.f;
     const float inv = any ? p.v_scale / L : 0.f;
     if (p.lse && grp == 0) p.lse[orow] = any ? (M + __log2f(L)) * kLn2 : kNegInf;
@@ -458,43 +616,8 @@ __global__ __launch_bounds__(kWaves * kWave) void qsa_attn_kernel(AttnParams p) 
     for (int k = 0; k < 4; ++k)
 #pragma unroll
       for (int j = 0; j < G::kPV; ++j) vals[k * G::kPV + j] = o[j][k] * inv;
-    const int64_t ob = orow * D + G::kOut * grp;
-    if (p.out_dtype == kDtFP32) {
-      float4* dst = reinterpret_cast<float4*>(static_cast<float*>(p.out) + ob);
-#pragma unroll
-      for (int i = 0; i < G::kOut / 4; ++i)
-        dst[i] = float4{vals[4 * i], vals[4 * i + 1], vals[4 * i + 2], vals[4 * i + 3]};
-    } else if (p.out_dtype == kDtBF16) {
-      u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.out) + ob);
-#pragma unroll
-      for (int i = 0; i < G::kOut / 8; ++i) {
-        u32x4 v;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          bf16x2 b;
-          b[0] = (__bf16)vals[8 * i + 2 * k];
-          b[1] = (__bf16)vals[8 * i + 2 * k + 1];
-          v[k] = bitcast<uint32_t>(b);
-        }
-        dst[i] = v;
-      }
-    } else {
-      u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.out) + ob);
-#pragma unroll
-      for (int i = 0; i < G::kOut / 8; ++i) {
-        u32x4 v;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          f16x2 h;
-          h[0] = (_Float16)vals[8 * i + 2 * k];
-          h[1] = (_Float16)vals[8 * i + 2 * k + 1];
-          v[k] = bitcast<uint32_t>(h);
-        }
-        dst[i] = v;
-      }
-    }
+    store_row<G::kOut>(p.out, p.out_dtype, orow * D + G::kOut * grp, vals);
   } else {
-    if (!head_ok) return;
     const int64_t pi = orow * p.num_splits + part;
     if (grp == 0) {
       p.ws_ml[2 * pi] = M;
@@ -510,16 +633,48 @@ __global__ __launch_bounds__(kWaves * kWave) void qsa_attn_kernel(AttnParams p) 
   }
 }
 
+// 16-token tiles ask for two waves per SIMD (<= 256 registers per wave);
+// 32-token tiles keep more rows in flight per wave at one wave per SIMD.
+template <int KIND, int D>
+__global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void qsa_attn16_kernel(AttnParams p) {
+  attn_body<KIND, D, 16>(p);
+}
+template <int KIND, int D>
+__global__ __launch_bounds__(kWaves * kWave) void qsa_attn32_kernel(AttnParams p) {
+  attn_body<KIND, D, 32>(p);
+}
+
 // Log-sum-exp merge of the split-K partials of one (row, head) per wave:
-// M = max M_p, L = sum L_p 2^(M_p - M), out = sum o_p 2^(M_p - M) / L, times
-// the E4M3 V scale (applied once, after the merge).
+// M = max_p m_p, L = sum_p L_p 2^(m_p - M), out = sum_p o_p 2^(m_p - M) / L,
+// times the E4M3 V scale (applied once, after the merge).  Each lane owns
+// D/64 outputs; the first partials are loaded together with the (max, sum)
+// pairs, so the call costs about one memory round trip.
 template <int D>
 __global__ __launch_bounds__(kWave) void qsa_merge_kernel(AttnParams p) {
   constexpr int E = D / kWave;
+  constexpr int kPre = 8;
   const int lane = lane_id();
   const int64_t rh = blockIdx.x;   // r * Hq + h
   const int P = p.num_splits;
   const int64_t base = rh * P;
+  const float* src = p.ws_o + base * D + lane * E;
+  float pre[kPre][E];
+#pragma unroll
+  for (int q = 0; q < kPre; ++q) {
+    if (q < P) {
+      if constexpr (E == 4) {
+        const float4 v = *reinterpret_cast<const float4*>(src + (int64_t)q * D);
+        pre[q][0] = v.x; pre[q][1] = v.y; pre[q][2] = v.z; pre[q][3] = v.w;
+      } else {
+        const float2 v = *reinterpret_cast<const float2*>(src + (int64_t)q * D);
+        pre[q][0] = v.x; pre[q][1] = v.y;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < E; ++i) pre[q][i] = 0.f;
+    }
+  }
   float mp = kNegInf, lp = 0.f;
   if (lane < P) {
     mp = p.ws_ml[2 * (base + lane)];
@@ -531,16 +686,16 @@ __global__ __launch_bounds__(kWave) void qsa_merge_kernel(AttnParams p) {
   float acc[E];
 #pragma unroll
   for (int i = 0; i < E; ++i) acc[i] = 0.f;
-  for (int q = 0; q < P; ++q) {
+#pragma unroll
+  for (int q = 0; q < kPre; ++q) {
     const float fq = __shfl(f, q);
-    const float* src = p.ws_o + (base + q) * D + lane * E;
-    if constexpr (E == 4) {
-      const float4 v = *reinterpret_cast<const float4*>(src);
-      acc[0] += fq * v.x; acc[1] += fq * v.y; acc[2] += fq * v.z; acc[3] += fq * v.w;
-    } else {
-      const float2 v = *reinterpret_cast<const float2*>(src);
-      acc[0] += fq * v.x; acc[1] += fq * v.y;
-    }
+#pragma unroll
+    for (int i = 0; i < E; ++i) acc[i] += fq * pre[q][i];
+  }
+  for (int q = kPre; q < P; ++q) {
+    const float fq = __shfl(f, q);
+#pragma unroll
+    for (int i = 0; i < E; ++i) acc[i] += fq * src[(int64_t)q * D + i];
   }
   const bool any = L > 0.f;
   const float inv = any ? p.v_scale / L : 0.f;
@@ -561,15 +716,33 @@ __global__ __launch_bounds__(kWave) void qsa_merge_kernel(AttnParams p) {
   }
 }
 
-template <int KIND>
-hipError_t launch_kind(int head_dim, const AttnParams& p, hipStream_t s) {
+// Tokens per tile.  16 keeps every (kind, D) within 256 registers at two
+// waves per SIMD, except bf16 at D = 256, whose 32-byte-per-element tiles
+// would spill there; it takes 32-token tiles at one wave per SIMD instead.
+// A tuning build may force one size with -DQSAKV_TILE=16|32.
+template <int KIND, int D>
+constexpr int tile_tokens() {
+#ifdef QSAKV_TILE
+  return QSAKV_TILE;
+#else
+  return (KIND == kBF16 && D == 256) ? 32 : 16;
+#endif
+}
+
+template <int KIND, int D>
+hipError_t launch_kd(const AttnParams& p, hipStream_t s) {
   const unsigned grid = (unsigned)(p.num_rows * p.num_kv_heads * p.num_splits);
   const dim3 block(kWaves * kWave);
-  if (head_dim == 256)
-    qsa_attn_kernel<KIND, 256><<<grid, block, 0, s>>>(p);
+  if constexpr (tile_tokens<KIND, D>() == 16)
+    qsa_attn16_kernel<KIND, D><<<grid, block, 0, s>>>(p);
   else
-    qsa_attn_kernel<KIND, 128><<<grid, block, 0, s>>>(p);
+    qsa_attn32_kernel<KIND, D><<<grid, block, 0, s>>>(p);
   return hipGetLastError();
+}
+
+template <int KIND>
+hipError_t launch_kind(int head_dim, const AttnParams& p, hipStream_t s) {
+  return head_dim == 256 ? launch_kd<KIND, 256>(p, s) : launch_kd<KIND, 128>(p, s);
 }
 
 }  // namespace

@@ -131,16 +131,25 @@ qsakv::AttnParams make_params(const qkv_cache* c, const qsa_args* a, int32_t spl
   return p;
 }
 
-size_t ws_bytes(int64_t rows, int64_t heads, int64_t d, int64_t splits) {
-  if (rows < 0 || heads <= 0 || (d != 128 && d != 256) || splits < 1 || splits > 64) return 0;
-  if (splits == 1) return 0;
-  int64_t n;
-  if (!mul_ok(rows, heads, &n) || !mul_ok(n, splits, &n)) return 0;
+// Workspace layout: [R*Hq*P*D fp32 partials | pad to 256 B]
+// [R*Hq*P*2 fp32 (max, sum)].
+struct WsLayout {
   int64_t o_bytes, ml_bytes;
-  if (!mul_ok(n, d * 4, &o_bytes) || !mul_ok(n, 8, &ml_bytes)) return 0;
-  o_bytes = (o_bytes + 255) / 256 * 256;
-  if (o_bytes > kI64Max - ml_bytes) return 0;
-  return (size_t)(o_bytes + ml_bytes);
+};
+
+bool ws_layout(int64_t rows, int64_t heads, int64_t d, int64_t splits, WsLayout* l) {
+  if (rows < 0 || heads <= 0 || (d != 128 && d != 256) || splits < 1 || splits > 64) return false;
+  int64_t n, rh;
+  if (!mul_ok(rows, heads, &rh) || !mul_ok(rh, splits, &n)) return false;
+  if (!mul_ok(n, d * 4, &l->o_bytes) || !mul_ok(n, 8, &l->ml_bytes)) return false;
+  l->o_bytes = (l->o_bytes + 255) / 256 * 256;
+  return l->o_bytes <= kI64Max - l->ml_bytes;
+}
+
+size_t ws_bytes(int64_t rows, int64_t heads, int64_t d, int64_t splits) {
+  WsLayout l;
+  if (!ws_layout(rows, heads, d, splits, &l) || splits == 1) return 0;
+  return (size_t)(l.o_bytes + l.ml_bytes);
 }
 
 }  // namespace
@@ -212,11 +221,12 @@ qkv_status qsa_sparse_attn_decode(const qkv_cache* cache, const qsa_args* args, 
     return finish(qsakv::launch_attn(cache->kind, cache->head_dim, p, s));
   const size_t need = ws_bytes(args->num_rows, args->num_q_heads, cache->head_dim, num_splits);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return QKV_ERR_WORKSPACE;
-  const int64_t n = (int64_t)args->num_rows * args->num_q_heads * num_splits;
-  const int64_t o_bytes = (n * cache->head_dim * 4 + 255) / 256 * 256;
-  p.ws_o = static_cast<float*>(workspace);
-  p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
-  hipError_t e = qsakv::launch_attn(cache->kind, cache->head_dim, p, s);
+  WsLayout l;
+  ws_layout(args->num_rows, args->num_q_heads, cache->head_dim, num_splits, &l);
+  char* ws = static_cast<char*>(workspace);
+  p.ws_o = reinterpret_cast<float*>(ws);
+  p.ws_ml = reinterpret_cast<float*>(ws + l.o_bytes);
+  const hipError_t e = qsakv::launch_attn(cache->kind, cache->head_dim, p, s);
   if (e != hipSuccess) return finish(e);
   return finish(qsakv::launch_merge(cache->head_dim, p, s));
 }

@@ -57,31 +57,13 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
 
 // Two signed int8 codes in bytes (b_lo, b_hi) of `x` -- already XOR-ed with
 // 0x80 so that each byte holds q + 128 -- become the fp16 pair
-// (q_lo, q_hi): 0x64XX is the fp16 value 1024 + XX, exact for XX < 256, and
-// subtracting 1152 leaves q exactly (|q| <= 127 fits fp16's 11-bit
-// significand).
+// (1152 + q_lo, 1152 + q_hi): 0x64XX is the fp16 value 1024 + XX, exact for
+// XX < 256.  The constant 1152 is removed after the dot product.
 __device__ __forceinline__ uint32_t i8pair_to_f16x2(uint32_t x_biased, uint32_t sel) {
   return perm(0x64646464u, x_biased, sel);
 }
 constexpr uint32_t kSelB01 = 0x04010400u;  // bytes 0,1 -> (0x64b0, 0x64b1)
 constexpr uint32_t kSelB23 = 0x04030402u;  // bytes 2,3 -> (0x64b2, 0x64b3)
-
-__device__ __forceinline__ f16x8 sub1152(u32x4 w) {
-  const f16x8 bias = {1152, 1152, 1152, 1152, 1152, 1152, 1152, 1152};
-  return bitcast<f16x8>(w) - bias;
-}
-
-// Eight int8 codes (two little-endian words, element order preserved) ->
-// eight exact fp16 values.
-__device__ __forceinline__ f16x8 i8x8_to_f16(uint32_t w0, uint32_t w1) {
-  const uint32_t x0 = w0 ^ 0x80808080u, x1 = w1 ^ 0x80808080u;
-  u32x4 r;
-  r[0] = i8pair_to_f16x2(x0, kSelB01);
-  r[1] = i8pair_to_f16x2(x0, kSelB23);
-  r[2] = i8pair_to_f16x2(x1, kSelB01);
-  r[3] = i8pair_to_f16x2(x1, kSelB23);
-  return sub1152(r);
-}
 
 // Two OCP E4M3FN codes in the low (hi_word = false) or high 16 bits of w ->
 // two exact fp16 values (every E4M3 value is representable in fp16), using
@@ -91,15 +73,6 @@ __device__ __forceinline__ uint32_t e4m3pair_to_f16x2(uint32_t w) {
   f16x2 h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, kHiWord);
   return bitcast<uint32_t>(h);
 }
-__device__ __forceinline__ f16x8 e4m3x8_to_f16(uint32_t w0, uint32_t w1) {
-  u32x4 r;
-  r[0] = e4m3pair_to_f16x2<false>(w0);
-  r[1] = e4m3pair_to_f16x2<true>(w0);
-  r[2] = e4m3pair_to_f16x2<false>(w1);
-  r[3] = e4m3pair_to_f16x2<true>(w1);
-  return bitcast<f16x8>(r);
-}
-
 // ---------------------------------------------------------------------------
 // MFMA 16x16x32 (fp16 / bf16 inputs, fp32 accumulate)
 //   A (16 x 32): lane l holds row l%16, k-slots 8*(l/16) .. +7

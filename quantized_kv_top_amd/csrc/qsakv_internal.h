@@ -58,8 +58,8 @@ struct AttnParams {
   int32_t chunk;          // ceil(topk / P)
 };
 
-// One pass over every (row, KV head, partition); P == 1 writes out/lse,
-// P > 1 writes the partials, then launch_merge combines them.
+// One pass over every (row, KV head, partition); P == 1 writes out/lse
+// directly, P > 1 writes partials that launch_merge combines.
 hipError_t launch_attn(int kind, int head_dim, const AttnParams& p, hipStream_t s);
 hipError_t launch_merge(int head_dim, const AttnParams& p, hipStream_t s);
 

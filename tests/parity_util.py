@@ -97,7 +97,7 @@ def run_attention(c, w, num_splits=1, out_dtype=None, lse=True, decode=None, top
     use_decode = (num_splits != 1) if decode is None else decode
     if use_decode:
         nb = qsakv.qsa_decode_workspace_bytes(R, Hq, D, num_splits)
-        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(max(nb, 1), dtype=torch.uint8, device="cuda")
         qsakv.qsa_sparse_attn_decode(c, q, rs, bt, idx, sm, out, num_splits, ws, lse=lse_t)
     else:
         qsakv.qsa_sparse_attn_prefill(c, q, rs, bt, idx, sm, out, lse=lse_t)

@@ -59,7 +59,9 @@ def test_cache_bytes_match_oracle_layout(kind, D):
 def test_workspace_bytes():
     L = qsakv.lib()
     n = 40 * 16 * 8
+    # the partials (padded to 256 B), then (max, sum) pairs
     assert L.qsa_decode_workspace_bytes(40, 16, 256, 8) == n * 256 * 4 + n * 8
+    assert L.qsa_decode_workspace_bytes(3, 4, 128, 2) == 24 * 512 + 24 * 8
     assert L.qsa_decode_workspace_bytes(40, 16, 256, 1) == 0
     assert L.qsa_decode_workspace_bytes(40, 16, 64, 8) == 0
     assert L.qsa_decode_workspace_bytes(40, 16, 256, 65) == 0

@@ -281,3 +281,27 @@ def test_e4m3_scale_folding():
     ob, lb = run_attention(b, w, out_dtype="fp32", sm_scale=w.sm_scale * ks)
     np.testing.assert_allclose(oa, vs * ob, rtol=1e-5, atol=1e-6)
     np.testing.assert_allclose(la, lb, rtol=1e-5, atol=1e-5)
+
+
+def test_decode_workspace_reuse():
+    """One workspace (contents arbitrary) serves repeated split-K calls, also
+    with fewer rows."""
+    w = small_workload(seed=43, topk=150, rows=6)
+    c, oc = _setup("int8", w)
+    ro, rl = oracle_attention(oc, w)
+    R, Hq, D = w.q.shape
+    nb = qsakv.qsa_decode_workspace_bytes(R, Hq, D, 8)
+    ws = torch.full((nb,), 0xA5, dtype=torch.uint8, device="cuda")
+    q = w.q.cuda()
+    rs = dev(w.row_seq, torch.int32)
+    bt = dev(w.block_table, torch.int32)
+    idx = dev(w.topk_idx, torch.int32)
+    for rows in (R, R, 3, R):
+        say("workspace reuse, rows", rows)
+        out = torch.full((rows, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+        lse = torch.full((rows, Hq), float("nan"), dtype=torch.float32, device="cuda")
+        qsakv.qsa_sparse_attn_decode(c, q[:rows].contiguous(), rs[:rows].contiguous(), bt,
+                                     idx[:rows].contiguous(), w.sm_scale, out, 8, ws, lse=lse)
+        torch.cuda.synchronize()
+        check(out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
+              ro[:rows], rl[:rows], "reuse rows %d" % rows)
