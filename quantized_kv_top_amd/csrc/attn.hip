@@ -48,7 +48,6 @@
 namespace qsakv {
 namespace {
 
-constexpr int kWaves = 4;
 constexpr int kChunk = 1024;          // list positions resolved per LDS batch
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kMaxSlack = 8.f;      // log2 units the running max may lag behind
@@ -384,12 +383,14 @@ __device__ __forceinline__ void store_row(void* out, int out_dtype, int64_t off,
   }
 }
 
-template <int KIND, int D, int TT>
+template <int KIND, int D, int TT, int NW>
 __device__ __forceinline__ void attn_body(const AttnParams& p) {
   using G = Geo<KIND, D, TT>;
-  __shared__ float s_obuf[G::kOut * kWave];
-  __shared__ float s_m[kWaves][16], s_l[kWaves][16], s_sig[kWaves];
+  constexpr int kThreads = NW * kWave;
+  constexpr int kPer = kChunk / kThreads;   // positions resolved per thread and chunk
   __shared__ __align__(16) int s_slot[kChunk];
+  __shared__ float s_m[NW][16], s_l[NW][16];
+  __shared__ float s_obuf[NW / 2][G::kOut * kWave];
 
   const int lane = lane_id(), ln16 = lane & 15, grp = lane >> 4;
   const int w = threadIdx.x >> 6;
@@ -407,27 +408,43 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
   const int g = rg % p.num_kv_heads;
   const int r = rg / p.num_kv_heads;
   const int pbeg = min(part * p.chunk, p.topk);
-  const int pend = min(pbeg + p.chunk, p.topk);
-  const int seq = p.row_seq[r];
-  const bool seq_ok = seq >= 0 && seq < p.num_seqs;
-  const int npos = seq_ok ? pend - pbeg : 0;
+  const int nlist = min(pbeg + p.chunk, p.topk) - pbeg;
   const int32_t* idx_row = p.topk_idx + (int64_t)r * p.topk + pbeg;
-  const int32_t* bt_row = p.block_table + (int64_t)(seq_ok ? seq : 0) * p.bt_stride;
   const int bs_mask = (1 << p.log2_bs) - 1;
 
-  // ---- slots of the partition, resolved into LDS a chunk at a time --------
-  // (position -> block table -> slot; -1 for padding and for anything out of
-  // range).  Each thread resolves kChunk / 256 positions.
-  constexpr int kPer = kChunk / (kWaves * kWave);
+  // ---- the independent loads go out together: the row's sequence, the
+  // first chunk of list positions and the query --------------------------------
+  const int seq = p.row_seq[r];
   int cpos[kPer];
   auto chunk_start = [&](int c0) {
-    const int cn = min(kChunk, npos - c0);
+    const int cn = min(kChunk, nlist - c0);
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
-      const int i = threadIdx.x + u * kWaves * kWave;
+      const int i = threadIdx.x + u * kThreads;
       cpos[u] = i < cn ? idx_row[c0 + i] : -1;
     }
   };
+  if (nlist > 0) chunk_start(0);
+
+  const bool head_ok = ln16 < p.group;
+  const int hq = g * p.group + ln16;
+  u32x4 qraw[G::kQK];
+  {
+    const int64_t qoff = ((int64_t)r * p.num_q_heads + (head_ok ? hq : 0)) * D;
+    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + qoff;
+#pragma unroll
+    for (int i = 0; i < G::kQK; ++i) {
+      const int d0 = G::kOneByte ? 64 * (i >> 1) + 16 * grp + 8 * (i & 1) : 32 * i + 8 * grp;
+      qraw[i] = head_ok ? *reinterpret_cast<const u32x4*>(qrow + d0) : u32x4{0, 0, 0, 0};
+    }
+  }
+
+  // ---- slots of the partition, resolved into LDS a chunk at a time --------
+  // (position -> block table -> slot; -1 for padding and for anything out of
+  // range).
+  const bool seq_ok = seq >= 0 && seq < p.num_seqs;
+  const int npos = seq_ok ? nlist : 0;
+  const int32_t* bt_row = p.block_table + (int64_t)(seq_ok ? seq : 0) * p.bt_stride;
   auto chunk_finish = [&](int c0) {
     const int cn = min(kChunk, npos - c0);
     const int rounded = (cn + TT - 1) / TT * TT;
@@ -440,76 +457,64 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
     }
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
-      const int i = threadIdx.x + u * kWaves * kWave;
+      const int i = threadIdx.x + u * kThreads;
       const int pos = cpos[u];
       if (i < rounded)
         s_slot[i] = (blk[u] >= 0 && blk[u] < p.num_blocks) ? (blk[u] << p.log2_bs) + (pos & bs_mask)
                                                             : -1;
     }
   };
-  if (npos > 0) chunk_start(0);     // the index loads start before the query is read
+  if (npos > 0) chunk_finish(0);    // block-table loads in flight during the query setup
 
   // ---- Q operand (B of QK^T), the logit factor and the int8 bias term ----
-  const bool head_ok = ln16 < p.group;
-  const int hq = g * p.group + ln16;
   QOp<KIND> qop[G::kQK];
   float kfac, kbias = 0.f;
-  {
-    const int64_t qoff = ((int64_t)r * p.num_q_heads + (head_ok ? hq : 0)) * D;
-    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + qoff;
-    u32x4 raw[G::kQK];
+  if constexpr (KIND == kBF16) {
 #pragma unroll
-    for (int i = 0; i < G::kQK; ++i) {
-      const int d0 = G::kOneByte ? 64 * (i >> 1) + 16 * grp + 8 * (i & 1) : 32 * i + 8 * grp;
-      raw[i] = head_ok ? *reinterpret_cast<const u32x4*>(qrow + d0) : u32x4{0, 0, 0, 0};
-    }
-    if constexpr (KIND == kBF16) {
+    for (int i = 0; i < G::kQK; ++i) qop[i] = bitcast<bf16x8>(qraw[i]);
+    kfac = p.sm_log2e;
+  } else {
+    int e = 0;
+    if (p.q_dtype == kDtFP16) {
 #pragma unroll
-      for (int i = 0; i < G::kQK; ++i) qop[i] = bitcast<bf16x8>(raw[i]);
-      kfac = p.sm_log2e;
+      for (int i = 0; i < G::kQK; ++i) qop[i] = bitcast<f16x8>(qraw[i]);
     } else {
-      int e = 0;
-      if (p.q_dtype == kDtFP16) {
+      // bf16 queries: exact power-of-two prescale so max|q| lands in
+      // [2^14, 2^15), then round to fp16 (exact for every element >= 2^-14
+      // after scaling; smaller ones keep an absolute error <= 2^-25).
+      float amax = 0.f;
 #pragma unroll
-        for (int i = 0; i < G::kQK; ++i) qop[i] = bitcast<f16x8>(raw[i]);
-      } else {
-        // bf16 queries: exact power-of-two prescale so max|q| lands in
-        // [2^14, 2^15), then round to fp16 (exact for every element >= 2^-14
-        // after scaling; smaller ones keep an absolute error <= 2^-25).
-        float amax = 0.f;
+      for (int i = 0; i < G::kQK; ++i)
 #pragma unroll
-        for (int i = 0; i < G::kQK; ++i)
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            amax = fmaxf(amax, fabsf(__uint_as_float(raw[i][k] << 16)));
-            amax = fmaxf(amax, fabsf(__uint_as_float(raw[i][k] & 0xFFFF0000u)));
-          }
-        amax = group4_max(amax);
-        int ex = 0;
-        if (amax > 0.f) frexpf(amax, &ex);
-        e = amax > 0.f ? 15 - ex : 0;
-        e = e > 127 ? 127 : (e < -126 ? -126 : e);
-        const float sc = ldexpf(1.f, e);
-#pragma unroll
-        for (int i = 0; i < G::kQK; ++i) {
-          f16x8 h;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            h[2 * k] = (_Float16)(__uint_as_float(raw[i][k] << 16) * sc);
-            h[2 * k + 1] = (_Float16)(__uint_as_float(raw[i][k] & 0xFFFF0000u) * sc);
-          }
-          qop[i] = h;
+        for (int k = 0; k < 4; ++k) {
+          amax = fmaxf(amax, fabsf(__uint_as_float(qraw[i][k] << 16)));
+          amax = fmaxf(amax, fabsf(__uint_as_float(qraw[i][k] & 0xFFFF0000u)));
         }
-      }
-      kfac = p.sm_log2e * p.k_scale * ldexpf(1.f, -e);
-      if constexpr (G::kInt) {
-        float qs = 0.f;
+      amax = group4_max(amax);
+      int ex = 0;
+      if (amax > 0.f) frexpf(amax, &ex);
+      e = amax > 0.f ? 15 - ex : 0;
+      e = e > 127 ? 127 : (e < -126 ? -126 : e);
+      const float sc = ldexpf(1.f, e);
 #pragma unroll
-        for (int i = 0; i < G::kQK; ++i)
+      for (int i = 0; i < G::kQK; ++i) {
+        f16x8 h;
 #pragma unroll
-          for (int k = 0; k < 8; ++k) qs += (float)qop[i][k];
-        kbias = kI8Bias * group4_sum(qs);
+        for (int k = 0; k < 4; ++k) {
+          h[2 * k] = (_Float16)(__uint_as_float(qraw[i][k] << 16) * sc);
+          h[2 * k + 1] = (_Float16)(__uint_as_float(qraw[i][k] & 0xFFFF0000u) * sc);
+        }
+        qop[i] = h;
       }
+    }
+    kfac = p.sm_log2e * p.k_scale * ldexpf(1.f, -e);
+    if constexpr (G::kInt) {
+      float qs = 0.f;
+#pragma unroll
+      for (int i = 0; i < G::kQK; ++i)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) qs += (float)qop[i][k];
+      kbias = kI8Bias * group4_sum(qs);
     }
   }
 
@@ -523,14 +528,14 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
     if (c0 > 0) {
       __syncthreads();               // the previous chunk's slots are consumed
       chunk_start(c0);
+      chunk_finish(c0);
     }
-    chunk_finish(c0);
     __syncthreads();
     const int ntiles = (min(kChunk, npos - c0) + TT - 1) / TT;
-    const int my_n = ntiles > w ? (ntiles - w + kWaves - 1) / kWaves : 0;
-    // tiles w, w + 4, w + 8, ... of the chunk, kDepth of them in registers:
-    // kDepth - 1 in flight while one is computed
-    auto ts = [&](int k) { return s_slot + (w + kWaves * k) * TT; };
+    const int my_n = ntiles > w ? (ntiles - w + NW - 1) / NW : 0;
+    // tiles w, w + NW, w + 2 NW, ... of the chunk, kDepth of them in
+    // registers: kDepth - 1 in flight while one is computed
+    auto ts = [&](int k) { return s_slot + (w + NW * k) * TT; };
     TileRaw<KIND, D, TT> ta, tb, tc;
     if (my_n > 0) issue_tile<KIND, D, TT>(ta, p, g, ts(0));
     if (my_n > 1) issue_tile<KIND, D, TT>(tb, p, g, ts(1));
@@ -561,6 +566,10 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
   }
 
   // ---- merge the waves' partial results -----------------------------------
+  // Each wave brings its accumulator to the common max M (and, for int8, to
+  // scale 1 from its reference V scale); the waves are then summed pairwise
+  // in LDS, upper half onto lower half (a fixed order: bitwise
+  // reproducible), leaving the total in wave 0.
   const float l_h = group4_sum(st.l);
   if constexpr (G::kInt) {
     const float corr = kI8Bias * group4_sum(st.cw);
@@ -571,38 +580,41 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
     s_m[w][ln16] = st.m;
     s_l[w][ln16] = l_h;
   }
-  if (lane == 0) s_sig[w] = st.sig;
   __syncthreads();
   float M = kNegInf;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) M = fmaxf(M, s_m[i][ln16]);
+  for (int i = 0; i < NW; ++i) M = fmaxf(M, s_m[i][ln16]);
   float L = 0.f, myf = 0.f;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
+  for (int i = 0; i < NW; ++i) {
     const float mi = s_m[i][ln16];
     const float f = mi == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mi - M);
     L += f * s_l[i][ln16];
     if (i == w) myf = f;
   }
   if constexpr (G::kInt) myf *= st.sig;
-  for (int i = 0; i < kWaves - 1; ++i) {
-    if (w == i) {
+#pragma unroll
+  for (int j = 0; j < G::kPV; ++j) o[j] *= myf;
+#pragma unroll
+  for (int half = NW / 2; half >= 1; half >>= 1) {
+    if (w >= half && w < 2 * half) {
+      float* buf = s_obuf[w - half];
 #pragma unroll
       for (int j = 0; j < G::kPV; ++j)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int idx = (j * 4 + k) * kWave + lane;
-          const float v = myf * o[j][k];
-          s_obuf[idx] = i == 0 ? v : s_obuf[idx] + v;
-        }
+        for (int k = 0; k < 4; ++k) buf[(j * 4 + k) * kWave + lane] = o[j][k];
     }
     __syncthreads();
+    if (w < half) {
+      const float* buf = s_obuf[w];
+#pragma unroll
+      for (int j = 0; j < G::kPV; ++j)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[j][k] += buf[(j * 4 + k) * kWave + lane];
+    }
+    if (half > 1) __syncthreads();    // the next step overwrites these buffers
   }
-  if (w != kWaves - 1 || !head_ok) return;
-#pragma unroll
-  for (int j = 0; j < G::kPV; ++j)
-#pragma unroll
-    for (int k = 0; k < 4; ++k) o[j][k] = s_obuf[(j * 4 + k) * kWave + lane] + myf * o[j][k];
+  if (w != 0 || !head_ok) return;
 
   // lane (ln16, grp) holds d = (D/16) * (4*grp + k) + j for k < 4, j < D/16:
   // D/4 contiguous outputs starting at (D/4) * grp.
@@ -635,14 +647,14 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
 
 // 16-token tiles ask for two waves per SIMD (<= 256 registers per wave);
 // 32-token tiles keep more rows in flight per wave at one wave per SIMD.
-template <int KIND, int D>
-__global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int KIND, int D, int NW>
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void qsa_attn16_kernel(AttnParams p) {
-  attn_body<KIND, D, 16>(p);
+  attn_body<KIND, D, 16, NW>(p);
 }
-template <int KIND, int D>
-__global__ __launch_bounds__(kWaves * kWave) void qsa_attn32_kernel(AttnParams p) {
-  attn_body<KIND, D, 32>(p);
+template <int KIND, int D, int NW>
+__global__ __launch_bounds__(NW * kWave) void qsa_attn32_kernel(AttnParams p) {
+  attn_body<KIND, D, 32, NW>(p);
 }
 
 // Log-sum-exp merge of the split-K partials of one (row, head) per wave:
@@ -729,15 +741,31 @@ constexpr int tile_tokens() {
 #endif
 }
 
+// Waves per workgroup.  A workgroup's fixed cost is a chain of dependent
+// memory round trips (list positions, block table, first tile, partial
+// store), so launches with few items spread each item over more waves and
+// run in one wave of workgroups where they can: at two waves per SIMD the
+// chip holds 2048 waves.  Large launches (prefill) keep 4 waves per item.
+template <int KIND, int D, int NW>
+hipError_t launch_knw(const AttnParams& p, unsigned grid, hipStream_t s) {
+  if constexpr (tile_tokens<KIND, D>() == 16)
+    qsa_attn16_kernel<KIND, D, NW><<<grid, dim3(NW * kWave), 0, s>>>(p);
+  else
+    qsa_attn32_kernel<KIND, D, NW><<<grid, dim3(NW * kWave), 0, s>>>(p);
+  return hipGetLastError();
+}
+
 template <int KIND, int D>
 hipError_t launch_kd(const AttnParams& p, hipStream_t s) {
-  const unsigned grid = (unsigned)(p.num_rows * p.num_kv_heads * p.num_splits);
-  const dim3 block(kWaves * kWave);
-  if constexpr (tile_tokens<KIND, D>() == 16)
-    qsa_attn16_kernel<KIND, D><<<grid, block, 0, s>>>(p);
-  else
-    qsa_attn32_kernel<KIND, D><<<grid, block, 0, s>>>(p);
-  return hipGetLastError();
+  const int64_t items = (int64_t)p.num_rows * p.num_kv_heads * p.num_splits;
+  const unsigned grid = (unsigned)items;
+  if constexpr (tile_tokens<KIND, D>() == 16) {   // two waves per SIMD
+    if (items <= 256) return launch_knw<KIND, D, 8>(p, grid, s);
+    if (items > 512 && items <= 1024) return launch_knw<KIND, D, 2>(p, grid, s);
+  } else {                                         // one wave per SIMD
+    if (items > 256 && items <= 512) return launch_knw<KIND, D, 2>(p, grid, s);
+  }
+  return launch_knw<KIND, D, 4>(p, grid, s);
 }
 
 template <int KIND>

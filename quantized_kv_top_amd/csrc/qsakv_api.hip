@@ -6,7 +6,7 @@
 #include <cstring>
 #include <limits>
 
-#include "../../include/qsakv.h"
+#include "qsakv.h"
 #include "qsakv_internal.h"
 
 namespace {

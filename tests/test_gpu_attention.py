@@ -94,6 +94,21 @@ def test_decode_splits(kind, P):
     check(o, l, ro, rl, "decode %s P%d" % (kind, P))
 
 
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("D", [128, 256])
+def test_workgroup_shapes(kind, D):
+    """40 rows x 2 KV heads x P partitions = 80 .. 1280 workgroup items: the
+    launch spreads an item over 8, 4 or 2 waves by item count, and every
+    shape must give the oracle's result."""
+    w = small_workload(seed=23, D=D, rows=40, topk=150)
+    c, oc = _setup(kind, w)
+    ro, rl = oracle_attention(oc, w)
+    for P in [1, 4, 8, 16]:
+        say("wg shapes", kind, D, "P", P)
+        o, l = run_attention(c, w, num_splits=P, decode=P > 1)
+        check(o, l, ro, rl, "wg shapes %s D%d P%d" % (kind, D, P))
+
+
 @pytest.mark.parametrize("G", [1, 4, 16])
 def test_group_sizes(G):
     w = small_workload(seed=13, Hq=2 * G, Hkv=2, D=128, topk=40)
