@@ -173,6 +173,7 @@ struct WaveState {
   float m;     // running max in use (log2 domain), per head
   float l;     // this lane's partial sum of exp2(logit - m)
   float sig;   // reference V scale (int8 kinds), wave-uniform
+  float rsig;  // 1 / sig (0 while sig is 0)
   float cw;    // this lane's partial sum of the PV weights (int8 bias removal)
 };
 
@@ -275,8 +276,9 @@ __device__ __forceinline__ void compute_tile(const TileRaw<KIND, D, TT>& t,
     if (smax > st.sig * kSigSlack) {     // the reference V scale moves (rare)
       beta *= st.sig / smax;
       st.sig = smax;
+      st.rsig = 1.f / smax;
     }
-    const float rs = st.sig > 0.f ? 1.f / st.sig : 0.f;
+    const float rs = st.rsig;
     float wsum = 0.f;
 #pragma unroll
     for (int e = 0; e < NT; ++e) {
@@ -390,7 +392,7 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
   constexpr int kPer = kChunk / kThreads;   // positions resolved per thread and chunk
   __shared__ __align__(16) int s_slot[kChunk];
   __shared__ float s_m[NW][16], s_l[NW][16];
-  __shared__ float s_obuf[NW / 2][G::kOut * kWave];
+  __shared__ f32x4 s_obuf[NW / 2][G::kPV * kWave];
 
   const int lane = lane_id(), ln16 = lane & 15, grp = lane >> 4;
   const int w = threadIdx.x >> 6;
@@ -519,7 +521,7 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
   }
 
   // ---- the wave's tiles -----------------------------------------------------
-  WaveState st{kNegInf, 0.f, 0.f, 0.f};
+  WaveState st{kNegInf, 0.f, 0.f, 0.f, 0.f};
   f32x4 o[G::kPV];
 #pragma unroll
   for (int j = 0; j < G::kPV; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -598,19 +600,15 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
 #pragma unroll
   for (int half = NW / 2; half >= 1; half >>= 1) {
     if (w >= half && w < 2 * half) {
-      float* buf = s_obuf[w - half];
+      f32x4* buf = s_obuf[w - half];
 #pragma unroll
-      for (int j = 0; j < G::kPV; ++j)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) buf[(j * 4 + k) * kWave + lane] = o[j][k];
+      for (int j = 0; j < G::kPV; ++j) buf[j * kWave + lane] = o[j];
     }
     __syncthreads();
     if (w < half) {
-      const float* buf = s_obuf[w];
+      const f32x4* buf = s_obuf[w];
 #pragma unroll
-      for (int j = 0; j < G::kPV; ++j)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) o[j][k] += buf[(j * 4 + k) * kWave + lane];
+      for (int j = 0; j < G::kPV; ++j) o[j] += buf[j * kWave + lane];
     }
     if (half > 1) __syncthreads();    // the next step overwrites these buffers
   }

@@ -36,15 +36,30 @@ __device__ __forceinline__ float wave_sum(float x) {
   for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
   return x;
 }
-// reduce across the four 16-lane groups that share lane & 15
-__device__ __forceinline__ float group4_max(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
+// Reduce across the four 16-lane groups that share lane & 15.  gfx950's
+// permlane swaps exchange 32-lane halves and odd/even 16-lane rows in the
+// VALU (no LDS round trip): called with the same value as both operands,
+// the pair returned holds x[l] and x[l ^ 32] (then x[l ^ 16]) in some order.
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float group4_sum(float x) {
-  x += __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
+__device__ __forceinline__ float xor16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float group4_max(float x) { return xor32_max(xor16_max(x)); }
+// the two pairings are summed in the same order on every lane, so all four
+// groups end with bitwise the same total
+__device__ __forceinline__ float group4_sum(float x) { return xor32_sum(xor16_sum(x)); }
 
 // ---------------------------------------------------------------------------
 // exact conversions of cache codes to MFMA operands
