@@ -311,6 +311,117 @@ def bench_e4m3(args):
                        "hbm_frac": b / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBPS}}
 
 
+class E2ELayer:
+    """One layer of the end-to-end step in its own 13.75 GiB pool: the
+    existing context written once; the chunk, its prefill and the decode
+    steps are what the timed loops run."""
+
+    def __init__(self, kind, seed):
+        per_block = sum(qsakv.cache_bytes(kind, 1, 64, 2, 256))
+        self.pool_blocks = wl.E2E_POOL_BYTES // per_block
+        e = wl.e2e(self.pool_blocks, device="cuda", seed=seed)
+        ks = vs = 1.0
+        if kind == "e4m3":
+            # per-layer scales max|x| / 448 over everything the layer holds
+            amax_k = torch.cat([e.ctx_k, e.chunk_k, e.step_k]).abs().max().float().item()
+            amax_v = torch.cat([e.ctx_v, e.chunk_v, e.step_v]).abs().max().float().item()
+            ks = float(np.float32(amax_k) / np.float32(448))
+            vs = float(np.float32(amax_v) / np.float32(448))
+        self.c = qsakv.Cache(kind, self.pool_blocks, 64, 2, 256, k_scale=ks, v_scale=vs,
+                             zero=False)
+        qsakv.kv_quant_write(self.c, e.ctx_k, e.ctx_v, torch.from_numpy(e.ctx_slots).cuda())
+        self.e = e
+        self.chunk_slots = torch.from_numpy(e.chunk_slots).cuda()
+        self.step_slots = torch.from_numpy(e.step_slots).cuda()
+        self.bt = torch.from_numpy(e.block_table).cuda()
+        self.rs_chunk = torch.zeros(e.chunk_q.shape[0], dtype=torch.int32, device="cuda")
+        self.rs_one = torch.zeros(1, dtype=torch.int32, device="cuda")
+        self.chunk_idx = torch.from_numpy(e.chunk_topk).cuda()
+        self.step_idx = [torch.from_numpy(e.step_topk[i:i + 1]).cuda()
+                         for i in range(e.step_topk.shape[0])]
+        self.chunk_out = torch.empty(e.chunk_q.shape, dtype=torch.bfloat16, device="cuda")
+        self.step_out = torch.empty((1,) + tuple(e.step_q.shape[1:]), dtype=torch.bfloat16,
+                                    device="cuda")
+        self.ws = torch.zeros(qsakv.qsa_decode_workspace_bytes(1, 16, 256, 8),
+                              dtype=torch.uint8, device="cuda")
+        e.ctx_k = e.ctx_v = None
+
+    def write_chunk(self, stream):
+        qsakv.kv_quant_write(self.c, self.e.chunk_k, self.e.chunk_v, self.chunk_slots,
+                             stream=stream)
+
+    def prefill(self, stream):
+        e = self.e
+        qsakv.qsa_sparse_attn_prefill(self.c, e.chunk_q, self.rs_chunk, self.bt, self.chunk_idx,
+                                      e.sm_scale, self.chunk_out, stream=stream)
+
+    def decode_steps(self, stream):
+        e = self.e
+        for i in range(len(self.step_idx)):
+            qsakv.kv_quant_write(self.c, e.step_k[i:i + 1], e.step_v[i:i + 1],
+                                 self.step_slots[i:i + 1], stream=stream)
+            qsakv.qsa_sparse_attn_decode(self.c, e.step_q[i:i + 1], self.rs_one, self.bt,
+                                         self.step_idx[i], e.sm_scale, self.step_out, 8,
+                                         self.ws, stream=stream)
+
+
+def bench_e2e(args):
+    """The end-to-end layer step of one 131K-token sequence in a 13.75 GiB
+    pool per cache kind: write an 8192-token chunk (quantize-on-write),
+    prefill its 8192 rows with top-k 1024, then 8 decode steps of [write one
+    token, attend with top-k 2048, split-K 8].  Each arm cycles over
+    ``--layers`` (default 2) independent layers, each with its own pool."""
+    stream = torch.cuda.current_stream()
+    L = args.layers or 2
+    arms = {}
+    for kind in ("int8", "bf16", "e4m3"):
+        log("building %d e2e layers (%s)" % (L, kind))
+        layers = [E2ELayer(kind, 5 + 100 * i) for i in range(L)]
+        for lay in layers:       # the step's inputs are device-resident before timing
+            lay.e.step_k, lay.e.step_v = lay.e.step_k.contiguous(), lay.e.step_v.contiguous()
+        e = layers[0].e
+        R, topk = e.chunk_q.shape[0], e.chunk_topk.shape[1]
+        torch.cuda.synchronize()
+        wr, _, _ = timed_loop(lambda i: layers[i % L].write_chunk(stream), args.steps,
+                              args.warmup, stream)
+        pf, _, _ = timed_loop(lambda i: layers[i % L].prefill(stream), args.steps,
+                              args.warmup, stream)
+        dc, _, _ = timed_loop(lambda i: layers[i % L].decode_steps(stream), args.steps,
+                              args.warmup, stream)
+        pf_ms, wr_ms, dc_ms = pf / args.steps, wr / args.steps, dc / args.steps
+        pb = R * gathered_bytes_per_row(kind, topk, 2, 256)
+        per_tok = sum(qsakv.cache_bytes(kind, 1, 64, 2, 256)) // 64
+        arms[kind] = {
+            "pool_blocks": int(layers[0].pool_blocks),
+            "pool_tokens": int(layers[0].pool_blocks) * 64,
+            "cache_bytes_per_token": int(per_tok),
+            "chunk_write_ms": wr_ms,
+            "chunk_prefill_ms": pf_ms,
+            "chunk_prefill_rows_per_s": R / (pf_ms / 1e3),
+            "chunk_prefill_gathered_GBps": pb / (pf_ms / 1e3) / 1e9,
+            "decode_8_steps_ms": dc_ms,
+            "layer_step_ms": wr_ms + pf_ms + dc_ms,
+        }
+        log("%s: write %.3f ms, prefill %.3f ms (%.0f GB/s), 8 decode steps %.3f ms" % (
+            kind, wr_ms, pf_ms, arms[kind]["chunk_prefill_gathered_GBps"], dc_ms))
+        del layers
+        torch.cuda.empty_cache()
+    for kind in arms:
+        arms[kind]["pool_tokens_vs_bf16"] = arms[kind]["pool_tokens"] / arms["bf16"]["pool_tokens"]
+    a = arms["int8"]
+    return {"metric": METRIC, "value": a["chunk_prefill_rows_per_s"], "unit": "rows/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": a["chunk_prefill_ms"], "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+            "config": {"workload": "e2e: one 131K-token sequence per layer in a 13.75 GiB pool "
+                                   "(Hq 16 / Hkv 2, D 256, block 64, bf16 Q/out); 8192-token "
+                                   "chunk write + prefill (top-k 1024) + 8 x [write 1 token, "
+                                   "decode top-k 2048, split-K 8]; %d layers rotated; value = "
+                                   "int8 chunk-prefill rows/s" % L,
+                       "arms": arms,
+                       "hbm_frac_int8_prefill": a["chunk_prefill_gathered_GBps"] / HBM_PEAK_GBPS}}
+
+
 def bench_write(args):
     stream = torch.cuda.current_stream()
     w = wl.decode(device="cuda", seed=300, num_seqs=2)
@@ -347,7 +458,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="prefill",
-                    choices=["prefill", "decode", "e4m3", "write", "copy"])
+                    choices=["prefill", "decode", "e4m3", "e2e", "write", "copy"])
     ap.add_argument("--layers", type=int, default=0)
     ap.add_argument("--splits", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -363,7 +474,7 @@ def main():
         sys.exit(2)
     qsakv.lib()
     fn = {"prefill": bench_prefill, "decode": bench_decode, "e4m3": bench_e4m3,
-          "write": bench_write, "copy": bench_copy}[args.config]
+          "e2e": bench_e2e, "write": bench_write, "copy": bench_copy}[args.config]
     print(json.dumps(fn(args)), flush=True)
 
 
