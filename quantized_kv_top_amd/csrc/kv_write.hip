@@ -1,7 +1,7 @@
 // Quantize-on-write of K/V rows into a paged cache.
 //
-// One wave per (token, KV head, K|V) row; each lane holds D/64 consecutive
-// elements.  The int8 arithmetic is the per-(token, head) symmetric rule of
+// Several (token, KV head) rows of K or of V per wave, 16 consecutive
+// elements per lane.  The int8 arithmetic is the per-(token, head) symmetric rule of
 // page "int8 per-(token,head) KV cache for the Qwen3.8-Flash-Next QSA path"
 // (section "Headline result"): a = max|x|, s = fl32(a / 127),
 // q = clamp(rne(fl32(x / s)), -127, 127), a zero row stores s = 0, q = 0.
@@ -16,40 +16,48 @@
 namespace qsakv {
 namespace {
 
-constexpr int kRowsPerBlock = 4;  // waves per workgroup
+// Work decomposition: K and V are two streams of rows (row = token * Hkv +
+// head, D elements each).  A wave takes kRPW consecutive rows of one stream
+// -- a contiguous span of the source -- with 16 elements per lane, kLPR lanes
+// per row; the row's max is reduced over its kLPR lanes.  The source and the
+// rows' slots are loaded together; stores are 16-byte (or dword, for the
+// 4-byte-aligned inline rows) per lane.
+constexpr int kEPL = 16;          // elements per lane
+constexpr int kWavesPerBlock = 4;
 
-template <int SRC, int E>
-__device__ __forceinline__ void load_src(const void* base, int64_t elem_off, float (&x)[E]) {
+template <int SRC>
+__device__ __forceinline__ void load_src16(const void* base, int64_t elem_off, float (&x)[kEPL]) {
   if constexpr (SRC == kDtFP32) {
-    const float* p = static_cast<const float*>(base) + elem_off;
-    if constexpr (E == 4) {
-      const float4 v = *reinterpret_cast<const float4*>(p);
-      x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
-    } else {
-      const float2 v = *reinterpret_cast<const float2*>(p);
-      x[0] = v.x; x[1] = v.y;
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem_off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 v = p[i];
+      x[4 * i] = v.x; x[4 * i + 1] = v.y; x[4 * i + 2] = v.z; x[4 * i + 3] = v.w;
     }
   } else {
-    const uint16_t* p = static_cast<const uint16_t*>(base) + elem_off;
-    uint32_t w[E / 2];
-    if constexpr (E == 4) {
-      const u32x2 v = *reinterpret_cast<const u32x2*>(p);
-      w[0] = v[0]; w[1] = v[1];
-    } else {
-      w[0] = *reinterpret_cast<const uint32_t*>(p);
-    }
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + elem_off);
+    const u32x4 w0 = p[0], w1 = p[1];
 #pragma unroll
-    for (int i = 0; i < E / 2; ++i) {
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t w = i < 4 ? w0[i] : w1[i - 4];
       if constexpr (SRC == kDtBF16) {
-        x[2 * i] = __uint_as_float(w[i] << 16);
-        x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        x[2 * i] = __uint_as_float(w << 16);
+        x[2 * i + 1] = __uint_as_float(w & 0xFFFF0000u);
       } else {
-        const f16x2 h = bitcast<f16x2>(w[i]);
+        const f16x2 h = bitcast<f16x2>(w);
         x[2 * i] = (float)h[0];
         x[2 * i + 1] = (float)h[1];
       }
     }
   }
+}
+
+// max over the kLPR lanes of a row (aligned groups of kLPR lanes)
+template <int kLPR>
+__device__ __forceinline__ float row_max(float a) {
+#pragma unroll
+  for (int o = kLPR / 2; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
+  return a;
 }
 
 // OCP E4M3FN encode of an fp32 value: round to nearest even, saturate to
@@ -75,92 +83,80 @@ __device__ __forceinline__ uint32_t e4m3_encode(float y) {
 }
 
 template <int KIND, int D, int SRC>
-__global__ __launch_bounds__(kRowsPerBlock * kWave) void kv_write_kernel(WriteParams p) {
-  constexpr int E = D / kWave;
+__global__ __launch_bounds__(kWavesPerBlock * kWave) void kv_write_kernel(WriteParams p) {
+  constexpr int kLPR = D / kEPL;         // lanes per row
+  constexpr int kRPW = kWave / kLPR;     // rows per wave
   const int lane = lane_id();
-  const int64_t rows = p.num_tokens * p.num_kv_heads * 2;
-  const int64_t stride = (int64_t)gridDim.x * kRowsPerBlock;
-  for (int64_t rw = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6); rw < rows;
-       rw += stride) {
-    const int64_t t = rw / (2 * p.num_kv_heads);
-    const int rem = (int)(rw - t * 2 * p.num_kv_heads);
-    const int h = rem >> 1;
-    const int which = rem & 1;  // 0 = K, 1 = V
+  const int sub = lane / kLPR, part = lane % kLPR;
+  const int hkv = p.num_kv_heads;
+  const int64_t nrow = p.num_tokens * hkv;                  // rows per stream
+  const int64_t gps = (nrow + kRPW - 1) / kRPW;             // wave groups per stream
+  const int64_t stride = (int64_t)gridDim.x * kWavesPerBlock;
+  for (int64_t gi = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6); gi < 2 * gps;
+       gi += stride) {
+    const int which = gi >= gps;                            // 0 = K, 1 = V
+    const int64_t r = (gi - which * gps) * kRPW + sub;
+    if (r >= nrow) continue;                                // whole rows drop out together
+    const int64_t t = r / hkv;
+    const int h = (int)(r - t * hkv);
     const int64_t slot = p.slot_mapping[t];
-    if (slot < 0 || slot >= p.num_slots) continue;  // wave-uniform
-
-    float x[E];
-    const int64_t src_off = (t * p.num_kv_heads + h) * D + lane * E;
-    load_src<SRC, E>(which ? p.v_src : p.k_src, src_off, x);
+    float x[kEPL];
+    load_src16<SRC>(which ? p.v_src : p.k_src, r * D + part * kEPL, x);
+    if (slot < 0 || slot >= p.num_slots) continue;
     uint8_t* base = which ? p.v : p.k;
-    const int64_t row = slot * p.num_kv_heads + h;
+    const int64_t row = slot * hkv + h;
 
     if constexpr (KIND == kInt8 || KIND == kInt8Inline) {
       float a = 0.f;
 #pragma unroll
-      for (int i = 0; i < E; ++i) a = fmaxf(a, fabsf(x[i]));
-      a = wave_max(a);
+      for (int i = 0; i < kEPL; ++i) a = fmaxf(a, fabsf(x[i]));
+      a = row_max<kLPR>(a);
       const float s = a / 127.0f;
-      uint32_t packed = 0;
+      uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int i = 0; i < E; ++i) {
+      for (int i = 0; i < kEPL; ++i) {
         float q = 0.f;
         if (s != 0.f) q = fminf(fmaxf(rintf(x[i] / s), -127.f), 127.f);
-        packed |= ((uint32_t)(int32_t)q & 0xFFu) << (8 * i);
+        w[i >> 2] |= ((uint32_t)(int32_t)q & 0xFFu) << (8 * (i & 3));
       }
-      constexpr int kRowBytes = (KIND == kInt8) ? D : D + 4;
-      uint8_t* dst = base + row * kRowBytes;
-      if constexpr (E == 4) {
-        *reinterpret_cast<uint32_t*>(dst + lane * 4) = packed;
-      } else {
-        *reinterpret_cast<uint16_t*>(dst + lane * 2) = (uint16_t)packed;
-      }
-      if (lane == 0) {
-        if constexpr (KIND == kInt8) {
-          p.kv_scale[row * 2 + which] = s;
-        } else {
-          *reinterpret_cast<float*>(dst + D) = s;
-        }
+      if constexpr (KIND == kInt8) {
+        *reinterpret_cast<u32x4*>(base + row * D + part * kEPL) = u32x4{w[0], w[1], w[2], w[3]};
+        if (part == 0) p.kv_scale[row * 2 + which] = s;
+      } else {  // 4-byte-aligned rows of D + 4 bytes
+        uint32_t* dst = reinterpret_cast<uint32_t*>(base + row * (D + 4) + part * kEPL);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[i] = w[i];
+        if (part == 0) *reinterpret_cast<float*>(base + row * (D + 4) + D) = s;
       }
     } else if constexpr (KIND == kE4M3) {
       const float scale = which ? p.v_scale : p.k_scale;
-      uint32_t packed = 0;
+      uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int i = 0; i < E; ++i) packed |= e4m3_encode(x[i] / scale) << (8 * i);
-      uint8_t* dst = base + row * D;
-      if constexpr (E == 4) {
-        *reinterpret_cast<uint32_t*>(dst + lane * 4) = packed;
-      } else {
-        *reinterpret_cast<uint16_t*>(dst + lane * 2) = (uint16_t)packed;
-      }
+      for (int i = 0; i < kEPL; ++i) w[i >> 2] |= e4m3_encode(x[i] / scale) << (8 * (i & 3));
+      *reinterpret_cast<u32x4*>(base + row * D + part * kEPL) = u32x4{w[0], w[1], w[2], w[3]};
     } else {  // kBF16: round to nearest even (identity for bf16 sources)
-      uint32_t w[E / 2];
+      uint32_t w[8];
 #pragma unroll
-      for (int i = 0; i < E / 2; ++i) {
+      for (int i = 0; i < 8; ++i) {
         bf16x2 b;
         b[0] = (__bf16)x[2 * i];
         b[1] = (__bf16)x[2 * i + 1];
         w[i] = bitcast<uint32_t>(b);
       }
-      uint8_t* dst = base + row * (2 * D) + lane * (2 * E);
-      if constexpr (E == 4) {
-        u32x2 v;
-        v[0] = w[0];
-        v[1] = w[1];
-        *reinterpret_cast<u32x2*>(dst) = v;
-      } else {
-        *reinterpret_cast<uint32_t*>(dst) = w[0];
-      }
+      u32x4* dst = reinterpret_cast<u32x4*>(base + row * (2 * D) + part * (2 * kEPL));
+      dst[0] = u32x4{w[0], w[1], w[2], w[3]};
+      dst[1] = u32x4{w[4], w[5], w[6], w[7]};
     }
   }
 }
 
 template <int KIND, int D>
 hipError_t launch_src(const WriteParams& p, hipStream_t s) {
-  const int64_t rows = p.num_tokens * p.num_kv_heads * 2;
-  const int64_t want = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  constexpr int kRPW = kWave / (D / kEPL);
+  const int64_t groups = 2 * ((p.num_tokens * p.num_kv_heads + kRPW - 1) / kRPW);
+  const int64_t want = (groups + kWavesPerBlock - 1) / kWavesPerBlock;
   const unsigned grid = (unsigned)(want < (1 << 20) ? want : (1 << 20));
-  const dim3 block(kRowsPerBlock * kWave);
+  const dim3 block(kWavesPerBlock * kWave);
   switch (p.src_dtype) {
     case kDtFP32: kv_write_kernel<KIND, D, kDtFP32><<<grid, block, 0, s>>>(p); break;
     case kDtBF16: kv_write_kernel<KIND, D, kDtBF16><<<grid, block, 0, s>>>(p); break;
