@@ -9,8 +9,9 @@ visits of the same cache.  Prints ONE JSON line.
 
 Other workloads (``--config``) print their own line for the record:
 decode (8 x 128K, 40 rows, top-k 2048, split-K 8), e4m3 (12 layers, 4 rows,
-top-k 2051, split-K 8 or 1), e2e (chunk write + prefill + 8 decode steps),
-write (quantize-on-write throughput).
+top-k 2051, split-K 8 or 1), mixed (12 E4M3 layers x a 46 + 1 + 1 + 1 row
+batch in one launch), e2e (chunk write + prefill + 8 decode steps), write
+(quantize-on-write throughput).
 """
 
 import argparse
@@ -311,6 +312,85 @@ def bench_e4m3(args):
                        "hbm_frac": b / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBPS}}
 
 
+class MixedLayer:
+    """An E4M3 layer read by a 46 + 1 + 1 + 1 row batch: either in one launch
+    or, as a row-routing reference, as two launches (the 46-row catch-up
+    chunk, then the three decode rows)."""
+
+    def __init__(self, layer, seed, splits):
+        w = wl.mixed_layer(layer, device="cuda", seed=seed)
+        ks = float(np.float32(w.k_src.abs().max().float().item()) / np.float32(448))
+        vs = float(np.float32(w.v_src.abs().max().float().item()) / np.float32(448))
+        self.w, self.splits = w, splits
+        self.c = qsakv.Cache("e4m3", w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim,
+                             k_scale=ks, v_scale=vs, zero=False)
+        qsakv.kv_quant_write(self.c, w.k_src, w.v_src, torch.from_numpy(w.slot_mapping).cuda())
+        w.k_src = w.v_src = None
+        self.bt = torch.from_numpy(w.block_table).cuda()
+        R, Hq, D = w.q.shape
+        self.parts = []
+        for lo, hi in ((0, R), (0, 46), (46, R)):
+            q = w.q[lo:hi].contiguous()
+            rs = torch.from_numpy(w.row_seq[lo:hi].copy()).cuda()
+            idx = torch.from_numpy(w.topk_idx[lo:hi].copy()).cuda()
+            out = torch.empty((hi - lo, Hq, D), dtype=torch.float16, device="cuda")
+            ws = torch.zeros(max(qsakv.qsa_decode_workspace_bytes(hi - lo, Hq, D, splits), 256),
+                             dtype=torch.uint8, device="cuda")
+            self.parts.append((q, rs, idx, out, ws))
+
+    def _call(self, i, stream):
+        q, rs, idx, out, ws = self.parts[i]
+        qsakv.qsa_sparse_attn_decode(self.c, q, rs, self.bt, idx, self.w.sm_scale, out,
+                                     self.splits, ws, stream=stream)
+
+    def one_launch(self, stream):
+        self._call(0, stream)
+
+    def two_launches(self, stream):
+        self._call(1, stream)
+        self._call(2, stream)
+
+
+class _Fn:
+    def __init__(self, fn):
+        self.fn = fn
+
+    def __call__(self, stream):
+        self.fn(stream)
+
+
+def bench_mixed(args):
+    """12 E4M3 layers, each read by a mixed batch of a 46-row catch-up chunk
+    plus three decode rows (the last with a shorter list), split-K
+    ``--splits``; one launch per layer vs the two-launch row routing."""
+    L = 12
+    sets = args.layers or 2
+    log("building %d x %d mixed-batch layers" % (L, sets))
+    layers = [MixedLayer(layer, 6 + 1000 * s, args.splits) for s in range(sets)
+              for layer in range(L)]
+    torch.cuda.synchronize()
+    one, _ = graph_loop([_Fn(x.one_launch) for x in layers], args.steps, args.warmup, 1)
+    two, _ = graph_loop([_Fn(x.two_launches) for x in layers], args.steps, args.warmup, 1)
+    w = layers[0].w
+    valid = int((w.topk_idx >= 0).sum())
+    b = L * valid * w.num_kv_heads * 2 * w.head_dim
+    ms1 = one / args.steps / sets
+    ms2 = two / args.steps / sets
+    return {"metric": METRIC, "value": L * w.num_rows / (ms1 / 1e3), "unit": "layer-rows/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms1,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "e4m3",
+            "data": "synthetic",
+            "config": {"workload": "mixed: 12 E4M3 layers (Hq 32 / Hkv 4, D 128, 64K ctx) x a "
+                                   "49-row batch = 46 catch-up rows + 3 decode rows (top-k 2051, "
+                                   "the last row 1500), split-K %d, one launch per layer; %d "
+                                   "independent 12-layer sets rotated, graph-captured"
+                                   % (args.splits, sets),
+                       "gathered_kv_bytes_per_step": b,
+                       "gathered_kv_GBps": b / (ms1 / 1e3) / 1e9,
+                       "two_launch_routing_ms_per_step": ms2,
+                       "two_launch_over_one": ms2 / ms1}}
+
+
 class E2ELayer:
     """One layer of the end-to-end step in its own 13.75 GiB pool: the
     existing context written once; the chunk, its prefill and the decode
@@ -475,7 +555,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="prefill",
-                    choices=["prefill", "decode", "e4m3", "e2e", "write", "copy"])
+                    choices=["prefill", "decode", "e4m3", "mixed", "e2e", "write", "copy"])
     ap.add_argument("--layers", type=int, default=0)
     ap.add_argument("--splits", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -491,7 +571,8 @@ def main():
         sys.exit(2)
     qsakv.lib()
     fn = {"prefill": bench_prefill, "decode": bench_decode, "e4m3": bench_e4m3,
-          "e2e": bench_e2e, "write": bench_write, "copy": bench_copy}[args.config]
+          "mixed": bench_mixed, "e2e": bench_e2e, "write": bench_write,
+          "copy": bench_copy}[args.config]
     print(json.dumps(fn(args)), flush=True)
 
 

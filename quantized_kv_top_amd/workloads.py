@@ -258,6 +258,34 @@ def e4m3_layer(layer, device="cpu", seed=4, num_seqs=4, ctx=65536, topk=2051,
                     extra={"layer": layer, "positions": np.full(num_seqs, ctx - 1)})
 
 
+def mixed_layer(layer, device="cpu", seed=6, ctx=65536, topk=2051, catch_up=46, decode_rows=3,
+                short_topk=1500):
+    """One E4M3 layer (the ``e4m3_layer`` cache and shapes) read by a mixed
+    batch in one launch: ``catch_up`` consecutive rows of sequence 0 ending
+    at its last position, then one decode row for each of the next
+    ``decode_rows`` sequences -- 46 + 1 + 1 + 1 = 49 rows by default.  Rows
+    have top-k ``topk`` except the last decode row, which lists only
+    ``short_topk`` positions followed by -1 padding (varlen lists)."""
+    w = e4m3_layer(layer, device=device, seed=seed, num_seqs=1 + decode_rows, ctx=ctx, topk=topk)
+    rng = np.random.default_rng([seed, layer, 7])
+    positions = np.concatenate([np.arange(ctx - catch_up, ctx), np.full(decode_rows, ctx - 1)])
+    row_seq = np.concatenate([np.zeros(catch_up, np.int32),
+                              np.arange(1, 1 + decode_rows, dtype=np.int32)])
+    R = positions.size
+    idx = np.full((R, topk), -1, np.int32)
+    for r in range(R):
+        n = short_topk if r == R - 1 else topk
+        idx[r, :n] = draw_sorted_distinct(rng, n, 0, int(positions[r]))
+    q = normal((R, w.num_q_heads, w.head_dim), seed * 100000 + layer * 10 + 5, device,
+               torch.float16)
+    w.name = "mixed"
+    w.q = q
+    w.row_seq = row_seq
+    w.topk_idx = idx
+    w.extra = {"layer": layer, "positions": positions}
+    return w
+
+
 @dataclass
 class E2EWorkload:
     """The end-to-end layer step: existing context, one prefill chunk, then

@@ -77,6 +77,25 @@ def test_e4m3_full_size(layer):
         check(o, l, ro, rl, "e4m3 layer %d P%d" % (layer, P))
 
 
+def test_mixed_catch_up_and_decode_rows_one_launch():
+    """A 49-row batch of 46 catch-up rows of one sequence plus three decode
+    rows of three others (the last with a shorter, padded list), E4M3 at the
+    E4M3 layer shape, in ONE launch -- split-K 1, 8 and 16 -- against the
+    oracle on every row."""
+    w = wl.mixed_layer(3, device="cuda")
+    ks, vs = e4m3_scales(w)
+    say("mixed 46+1+1+1: %d rows, scales %g %g" % (w.num_rows, ks, vs))
+    c = gpu_write("e4m3", w, ks, vs)
+    rows = np.arange(w.num_rows)
+    toks = needed_tokens(w, rows)
+    oc = oracle_write("e4m3", w, ks, vs, tokens=toks)
+    assert_rows_equal(c, oc, w.slot_mapping[toks])
+    ro, rl = oracle_attention(oc, w)
+    for P in (1, 8, 16):
+        o, l = run_attention(c, w, num_splits=P, decode=P > 1)
+        check(o, l, ro, rl, "mixed P%d" % P)
+
+
 @pytest.mark.parametrize("kind", ["int8", "e4m3", "bf16"])
 def test_e2e_layer_step(kind):
     """Existing context + an 8192-token chunk written (quantize-on-write) and

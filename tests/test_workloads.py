@@ -51,3 +51,16 @@ def test_student_t_heavy_tail():
     z = (x - x.mean()) / x.std()
     assert float((z ** 4).mean()) > 5.0
     assert abs(float(x.std()) - 0.5 * np.sqrt(2.0)) < 0.1
+
+
+def test_mixed_layer_structure():
+    w = wl.mixed_layer(0, ctx=4096, topk=300, short_topk=100)
+    assert w.num_rows == 49 and w.topk == 300
+    assert list(w.row_seq) == [0] * 46 + [1, 2, 3]
+    pos = w.extra["positions"]
+    assert list(pos[:46]) == list(range(4096 - 46, 4096)) and list(pos[46:]) == [4095] * 3
+    for r in range(49):
+        valid = w.topk_idx[r][w.topk_idx[r] >= 0]
+        assert valid.size == (100 if r == 48 else 300)
+        assert np.all(valid <= pos[r]) and np.unique(valid).size == valid.size
+    assert np.all(w.topk_idx[48, 100:] == -1)
