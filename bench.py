@@ -10,8 +10,9 @@ visits of the same cache.  Prints ONE JSON line.
 Other workloads (``--config``) print their own line for the record:
 decode (8 x 128K, 40 rows, top-k 2048, split-K 8), e4m3 (12 layers, 4 rows,
 top-k 2051, split-K 8 or 1), mixed (12 E4M3 layers x a 46 + 1 + 1 + 1 row
-batch in one launch), e2e (chunk write + prefill + 8 decode steps), write
-(quantize-on-write throughput).
+batch in one launch), e2e (chunk write + prefill + 8 decode steps), calib
+(E4M3 calibration statistics of 24 K/V tensors), write (quantize-on-write
+throughput).
 """
 
 import argparse
@@ -391,6 +392,42 @@ def bench_mixed(args):
                        "two_launch_over_one": ms2 / ms1}}
 
 
+def bench_calib(args):
+    """Calibration statistics of the E4M3 workload's 24 K/V source tensors
+    (12 layers x K, V; fp16 [4 x 65536][4][128] each, 268 MB) at their
+    envelope scales max|x| / 448: one kv_calib_stats call per tensor."""
+    stream = torch.cuda.current_stream()
+    tensors = []
+    log("building 12 E4M3 layers' K/V sources")
+    for layer in range(12):
+        w = wl.e4m3_layer(layer, device="cuda", seed=4)
+        for t in (w.k_src, w.v_src):
+            x = t.reshape(-1)
+            amax = float(x.abs().max().float().item())
+            tensors.append((x, float(np.float32(amax) / np.float32(448))))
+    out = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(qsakv.calib_workspace_bytes(), dtype=torch.uint8, device="cuda")
+    n = len(tensors)
+    total, per, _ = timed_loop(lambda i: qsakv.kv_calib_stats(tensors[i % n][0], tensors[i % n][1],
+                                                              out, ws, stream=stream),
+                               args.steps, args.warmup, stream)
+    ms = total / args.steps
+    b = tensors[0][0].numel() * 2
+    res = []
+    for x, sc in tensors[:2]:
+        qsakv.kv_calib_stats(x, sc, out, ws, stream=stream)
+        torch.cuda.synchronize()
+        res.append(qsakv.calib_result(out))
+    return {"metric": "calibration statistics GB/s (E4M3 K/V sources)", "value": b / (ms / 1e3) / 1e9,
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "fp16", "data": "synthetic",
+            "config": {"workload": "kv_calib_stats over 24 fp16 tensors of 134,217,728 "
+                                   "elements (12 layers x K, V), one call per tensor, rotated",
+                       "bytes_per_call": b, "hbm_frac": b / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
+                       "layer0_k": res[0], "layer0_v": res[1]}}
+
+
 class E2ELayer:
     """One layer of the end-to-end step in its own 13.75 GiB pool: the
     existing context written once; the chunk, its prefill and the decode
@@ -555,7 +592,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="prefill",
-                    choices=["prefill", "decode", "e4m3", "mixed", "e2e", "write", "copy"])
+                    choices=["prefill", "decode", "e4m3", "mixed", "e2e", "calib", "write",
+                             "copy"])
     ap.add_argument("--layers", type=int, default=0)
     ap.add_argument("--splits", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -571,7 +609,7 @@ def main():
         sys.exit(2)
     qsakv.lib()
     fn = {"prefill": bench_prefill, "decode": bench_decode, "e4m3": bench_e4m3,
-          "mixed": bench_mixed, "e2e": bench_e2e, "write": bench_write,
+          "mixed": bench_mixed, "e2e": bench_e2e, "calib": bench_calib, "write": bench_write,
           "copy": bench_copy}[args.config]
     print(json.dumps(fn(args)), flush=True)
 

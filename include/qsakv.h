@@ -217,6 +217,55 @@ QSAKV_API qkv_status qsa_sparse_attn_decode(const qkv_cache *cache, const qsa_ar
                                   void *stream);
 
 /*
+ * kv_calib_stats -- the per-tensor statistics that choose and audit an E4M3
+ * scale ([E4M3-PR] "Implementation scope": max-abs, p99.9, p99.99 and
+ * saturation per layer and tensor; "Why calibrated scale is part of this
+ * contract": at a given scale, the share of nonzero elements below E4M3's
+ * minimum subnormal 2^-9 and in the subnormal range below 2^-6;
+ * [SCALE-PACK] "Calibration": stored = e4m3fn(x / scale),
+ * scale = max envelope / 448).
+ *
+ *   x        device [n] of src_dtype (QKV_FP32, QKV_BF16 or QKV_FP16),
+ *            16-B aligned; any number of elements (the whole K or V
+ *            activation tensor of one layer).
+ *   scale    the E4M3 scale to evaluate: finite and >= FLT_MIN (1.0 is
+ *            legal), else QKV_ERR_BAD_SCALE.
+ *   out      device qkv_calib_result, 8-B aligned, written by the call.
+ *   workspace  device, >= qkv_calib_workspace_bytes(), 256-B aligned; its
+ *            contents on entry are ignored (the call clears what it uses);
+ *            calls sharing a workspace must not overlap in time.
+ * Definitions, with y = fl32(x / scale) (IEEE float32 division, as the
+ * converter): NaN elements are counted in `nan` and excluded from the rest;
+ * max_abs = max |x|; p999 / p9999 = nearest-rank percentiles of |x| over
+ * the non-NaN elements (zeros included): the k-th smallest with
+ * k = ceil(999 m / 1000), ceil(9999 m / 10000); saturated: |y| > 448;
+ * below_min_subnormal: x != 0 and |y| < 2^-9; subnormal: x != 0 and
+ * 2^-9 <= |y| < 2^-6.  All values are exact (counts, and float32 values
+ * that occur in x).  n = 0 writes zeros.  Launches: one streaming pass
+ * (per-workgroup histograms), a reduction, a selection; QKV_FP32 sources
+ * add a clearing pass, a second streaming pass and a second selection for
+ * the percentiles' low 16 bits.  The workspace is about 34 MB.
+ */
+typedef struct qkv_calib_result {
+  uint64_t count;               /* n                                        */
+  uint64_t nan;                 /* NaN elements                             */
+  uint64_t nonzero;             /* non-NaN elements != 0                    */
+  uint64_t saturated;           /* |y| > 448                                */
+  uint64_t below_min_subnormal; /* x != 0, |y| < 2^-9                       */
+  uint64_t subnormal;           /* x != 0, 2^-9 <= |y| < 2^-6               */
+  float max_abs;
+  float p999;
+  float p9999;
+  uint32_t reserved;
+} qkv_calib_result;
+
+QSAKV_API size_t qkv_calib_workspace_bytes(void);
+
+QSAKV_API qkv_status kv_calib_stats(const void *x, int32_t src_dtype, int64_t n, float scale,
+                                    qkv_calib_result *out, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+
+/*
  * qkv_cache_bytes -- sizes of the k, v and kv_scale tensors of a cache of
  * this kind and shape (scale_bytes = 0 for kinds without a side tensor).
  * Bytes per token, K + V, scales included: INT8 and INT8_INLINE

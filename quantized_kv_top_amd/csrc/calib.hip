@@ -1,0 +1,471 @@
+// Per-tensor calibration statistics of K/V activations at an E4M3 scale:
+// max-abs, nearest-rank p99.9 / p99.99 of |x|, and the counts of elements
+// whose converter quotient y = fl32(x / scale) saturates (|y| > 448), falls
+// below E4M3's minimum subnormal 2^-9, or lands in the subnormal range
+// [2^-9, 2^-6).  Page "[Model][SM70][FP8] Add calibrated E4M3 QSA KV cache"
+// (sections "Implementation scope" and "Why calibrated scale is part of
+// this contract"); the converter is that of page "Qwen3.8 Flash Next NVFP4
+// QSA FP8 E4M3 KV Scales" (section "Calibration").
+//
+// One streaming pass classifies every element by integer compares of its
+// float32 magnitude bits against thresholds the host derived from the same
+// float32 division (y is monotone in |x|), and builds a 32768-bin histogram
+// of a 15-bit magnitude key in LDS, which each workgroup stores to its own
+// slot (no contended global atomics); a reduction kernel sums the slots.
+// For fp16 and bf16 sources the key is
+// the source magnitude itself, so the percentile that a prefix scan of the
+// histogram finds is exact.  For fp32 sources the key is the top 15 bits of
+// the magnitude; a second streaming pass histograms the low 16 bits of the
+// elements in the two selected bins, and a second scan finishes the value.
+#include "qsakv_device.h"
+#include "qsakv_internal.h"
+
+namespace qsakv {
+namespace {
+
+constexpr int kBins = 32768;
+constexpr int kLowBins = 65536;
+constexpr int kPassThreads = 1024;
+constexpr int kSelThreads = 1024;
+constexpr int kMaxPass1 = 256;     // streaming workgroups (one per CU)
+
+constexpr int kRedThreads = 256;
+constexpr int kRedBlocks = kBins / kRedThreads;   // 128
+
+// Workspace, in uint64 words: [hist1 32768][hist2 2 x 65536][sel 8]
+// [per-workgroup counters 256 x 8][per-reduction-block counters 128 x 8],
+// then the per-workgroup uint32 histograms [256][32768].
+enum { kCntNan = 0, kCntNonzero, kCntSat, kCntBelow, kCntSub, kCntAmax, kCntBins = 7 };
+enum { kSelValid = 0, kSelB1, kSelR1, kSelB2, kSelR2 };
+constexpr int64_t kHeadWords = kBins + 2 * kLowBins + 8 + kMaxPass1 * 8 + kRedBlocks * 8;
+
+struct Ws {
+  unsigned long long* hist1;    // non-NaN elements per key
+  unsigned long long* hist2;
+  unsigned long long* sel;
+  unsigned long long* wg_cnt;   // [kMaxPass1][8]
+  unsigned long long* blk;      // [kRedBlocks][8]: counts, [kCntBins] = bins' sum
+  uint32_t* wg_hist;            // [kMaxPass1][kBins]
+};
+__device__ __forceinline__ Ws ws_of(const CalibParams& p) {
+  unsigned long long* w = static_cast<unsigned long long*>(p.workspace);
+  unsigned long long* c = w + kBins + 2 * kLowBins;
+  return Ws{w, w + kBins, c, c + 8, c + 8 + kMaxPass1 * 8,
+            reinterpret_cast<uint32_t*>(w + kHeadWords)};
+}
+
+// clears what the passes accumulate into with atomics (the fp32 low-bit
+// histograms); everything else is written whole
+__global__ __launch_bounds__(256) void calib_clear_kernel(CalibParams p) {
+  unsigned long long* h = ws_of(p).hist2;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < 2 * kLowBins;
+       i += (int64_t)gridDim.x * 256)
+    h[i] = 0ull;
+}
+
+struct Counts {
+  uint32_t nan = 0, nz = 0, sat = 0, below = 0, sub = 0, amax = 0;
+};
+
+
+__device__ __forceinline__ void classify(const CalibParams& p, uint32_t ab, uint32_t key,
+                                         uint32_t* s_hist, Counts& c) {
+  if (ab > 0x7F800000u) {
+    ++c.nan;
+    return;
+  }
+  atomicAdd(&s_hist[key], 1u);
+  c.amax = ab > c.amax ? ab : c.amax;
+  c.nz += ab != 0u;
+  c.sat += ab >= p.t_sat;
+  c.below += (ab != 0u) & (ab < p.t_sub);
+  c.sub += (ab >= p.t_sub) & (ab < p.t_norm);
+}
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint32_t y = __shfl_xor(x, o);
+    x = y > x ? y : x;
+  }
+  return x;
+}
+
+// Streaming pass.  fp16 / bf16: the 15-bit magnitude key is the value, so
+// only the histogram is built (NaN keys included) and every count follows
+// from it in the selection pass.  fp32: each element is also classified
+// here (NaN excluded from the histogram), and the key is the top 15 bits.
+template <int SRC>
+__global__ __launch_bounds__(kPassThreads) void calib_pass1_kernel(CalibParams p) {
+  __shared__ uint32_t s_hist[kBins];
+  __shared__ uint32_t s_cnt[kPassThreads / kWave][6];
+  for (int i = threadIdx.x; i < kBins; i += kPassThreads) s_hist[i] = 0u;
+  __syncthreads();
+  constexpr int kVec = 8;                          // elements per vector load
+  constexpr int kUnroll = 4;                       // vector loads in flight per thread
+  Counts c;
+  const int64_t nvec = p.n / kVec;
+  const int64_t stride = (int64_t)gridDim.x * kPassThreads;
+  for (int64_t v0 = (int64_t)blockIdx.x * kPassThreads + threadIdx.x; v0 < nvec;
+       v0 += stride * kUnroll) {
+    u32x4 raw[kUnroll][SRC == kDtFP32 ? 2 : 1];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t v = v0 + u * stride;
+      if (v >= nvec) break;
+      if constexpr (SRC == kDtFP32) {
+        raw[u][0] = static_cast<const u32x4*>(p.x)[2 * v];
+        raw[u][1] = static_cast<const u32x4*>(p.x)[2 * v + 1];
+      } else {
+        raw[u][0] = static_cast<const u32x4*>(p.x)[v];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (v0 + u * stride >= nvec) break;
+      if constexpr (SRC == kDtFP32) {
+#pragma unroll
+        for (int k = 0; k < kVec; ++k) {
+          const uint32_t ab = raw[u][k >> 2][k & 3] & 0x7FFFFFFFu;
+          classify(p, ab, ab >> 16, s_hist, c);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < kVec; k += 2) {
+          const uint32_t wd = raw[u][0][k >> 1];
+          atomicAdd(&s_hist[wd & 0x7FFFu], 1u);
+          atomicAdd(&s_hist[(wd >> 16) & 0x7FFFu], 1u);
+        }
+      }
+    }
+  }
+  // the n % 8 tail, one element per thread of the first workgroup
+  if (blockIdx.x == 0 && threadIdx.x < p.n - nvec * kVec) {
+    const int64_t i = nvec * kVec + threadIdx.x;
+    if constexpr (SRC == kDtFP32) {
+      const uint32_t ab = static_cast<const uint32_t*>(p.x)[i] & 0x7FFFFFFFu;
+      classify(p, ab, ab >> 16, s_hist, c);
+    } else {
+      atomicAdd(&s_hist[static_cast<const uint16_t*>(p.x)[i] & 0x7FFFu], 1u);
+    }
+  }
+  const Ws w = ws_of(p);
+  if constexpr (SRC == kDtFP32) {
+    // counters: waves -> LDS -> this workgroup's slot
+    const uint32_t nan = wave_sum_u32(c.nan), nz = wave_sum_u32(c.nz);
+    const uint32_t sat = wave_sum_u32(c.sat), below = wave_sum_u32(c.below);
+    const uint32_t sub = wave_sum_u32(c.sub), amax = wave_max_u32(c.amax);
+    const int wv = threadIdx.x >> 6;
+    if (lane_id() == 0) {
+      s_cnt[wv][kCntNan] = nan;
+      s_cnt[wv][kCntNonzero] = nz;
+      s_cnt[wv][kCntSat] = sat;
+      s_cnt[wv][kCntBelow] = below;
+      s_cnt[wv][kCntSub] = sub;
+      s_cnt[wv][kCntAmax] = amax;
+    }
+  }
+  __syncthreads();
+  u32x4* dst = reinterpret_cast<u32x4*>(w.wg_hist + (int64_t)blockIdx.x * kBins);
+  const u32x4* src = reinterpret_cast<const u32x4*>(s_hist);
+  for (int i = threadIdx.x; i < kBins / 4; i += kPassThreads) dst[i] = src[i];
+  if constexpr (SRC == kDtFP32) {
+    if (threadIdx.x < 6) {
+      unsigned long long v = 0;
+      for (int i = 0; i < kPassThreads / kWave; ++i) {
+        const unsigned long long x = s_cnt[i][threadIdx.x];
+        v = threadIdx.x == kCntAmax ? (x > v ? x : v) : v + x;
+      }
+      w.wg_cnt[blockIdx.x * 8 + threadIdx.x] = v;
+    }
+  }
+}
+
+// float32 magnitude bits of a 16-bit key (NaN keys map to a float32 NaN)
+__device__ __forceinline__ uint32_t key_bits(int src_dtype, uint32_t key) {
+  if (src_dtype == kDtBF16) return key << 16;
+  if (key > 0x7C00u) return 0x7FC00000u;
+  return __float_as_uint(fabsf((float)bitcast<_Float16>((uint16_t)key)));
+}
+
+template <int N>
+__device__ __forceinline__ void block_reduce6(unsigned long long (&v)[N],
+                                              unsigned long long (*s_red)[N]) {
+  const int wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int f = 0; f < N; ++f) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const unsigned long long y = __shfl_xor(v[f], o);
+      v[f] = f == kCntAmax ? (y > v[f] ? y : v[f]) : v[f] + y;
+    }
+    if (lane_id() == 0) s_red[wv][f] = v[f];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int f = 0; f < N; ++f) {
+    unsigned long long x = 0;
+    for (int i = 0; i < (int)(blockDim.x / kWave); ++i)
+      x = f == kCntAmax ? (s_red[i][f] > x ? s_red[i][f] : x) : x + s_red[i][f];
+    v[f] = x;
+  }
+}
+
+// One thread per key: hist1[key] = the workgroups' slots summed (16 slots in
+// flight per thread), NaN keys of 16-bit sources set aside; each block then
+// leaves its counts (16-bit sources: classified per key, exact since the key
+// is the value) and the sum of its bins for the selection.
+__global__ __launch_bounds__(kRedThreads) void calib_reduce_kernel(CalibParams p) {
+  __shared__ unsigned long long s_red[kRedThreads / kWave][8];
+  const Ws w = ws_of(p);
+  const uint32_t key = blockIdx.x * kRedThreads + threadIdx.x;
+  constexpr int kIn = 16;
+  unsigned long long h = 0;
+  for (int g0 = 0; g0 < p.grid1; g0 += kIn) {
+    uint32_t v[kIn];
+#pragma unroll
+    for (int u = 0; u < kIn; ++u)
+      v[u] = g0 + u < p.grid1 ? w.wg_hist[(int64_t)(g0 + u) * kBins + key] : 0u;
+#pragma unroll
+    for (int u = 0; u < kIn; ++u) h += v[u];
+  }
+  unsigned long long c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (p.src_dtype != kDtFP32) {
+    const uint32_t ab = key_bits(p.src_dtype, key);
+    if (ab > 0x7F800000u) {
+      c[kCntNan] = h;
+      h = 0;
+    } else {
+      c[kCntNonzero] = ab != 0u ? h : 0ull;
+      c[kCntSat] = ab >= p.t_sat ? h : 0ull;
+      c[kCntBelow] = (ab != 0u && ab < p.t_sub) ? h : 0ull;
+      c[kCntSub] = (ab >= p.t_sub && ab < p.t_norm) ? h : 0ull;
+      c[kCntAmax] = h ? ab : 0u;
+    }
+  } else if (blockIdx.x == 0 && threadIdx.x < 6) {
+    // fp32: the streaming pass classified the elements; sum its counters
+    // (one field per thread, then spread through the block reduction)
+    for (int g = 0; g < p.grid1; ++g) {
+      const unsigned long long x = w.wg_cnt[g * 8 + threadIdx.x];
+      c[threadIdx.x] = threadIdx.x == kCntAmax ? (x > c[threadIdx.x] ? x : c[threadIdx.x])
+                                               : c[threadIdx.x] + x;
+    }
+  }
+  w.hist1[key] = h;
+  c[kCntBins] = h;
+  block_reduce6<8>(c, s_red);
+  if (threadIdx.x < 8) w.blk[blockIdx.x * 8 + threadIdx.x] = c[threadIdx.x];
+}
+
+// Exclusive prefix sum of one value per thread over the block (s_tmp holds
+// one word per wave), and the block total.
+__device__ __forceinline__ unsigned long long block_exscan(unsigned long long v,
+                                                           unsigned long long* s_tmp,
+                                                           unsigned long long& total) {
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  unsigned long long inc = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const unsigned long long y = __shfl_up(inc, o);
+    if (lane >= o) inc += y;
+  }
+  if (lane == kWave - 1) s_tmp[w] = inc;
+  __syncthreads();
+  unsigned long long before = 0, all = 0;
+  for (int i = 0; i < (int)(blockDim.x / kWave); ++i) {
+    if (i < w) before += s_tmp[i];
+    all += s_tmp[i];
+  }
+  __syncthreads();
+  total = all;
+  return before + inc - v;
+}
+
+// Find, among `bins` bins of which each thread owns `per` consecutive ones,
+// the bin holding 1-based rank k and the rank left inside that bin.
+__device__ __forceinline__ void find_rank(const unsigned long long* hist, int per,
+                                          unsigned long long excl, unsigned long long k,
+                                          unsigned long long* s_out) {
+  unsigned long long mine = 0;
+  for (int i = 0; i < per; ++i) mine += hist[threadIdx.x * per + i];
+  if (k > excl && k <= excl + mine) {
+    unsigned long long cum = excl;
+    for (int i = 0; i < per; ++i) {
+      const unsigned long long h = hist[threadIdx.x * per + i];
+      if (cum + h >= k) {
+        s_out[0] = (unsigned long long)(threadIdx.x * per + i);
+        s_out[1] = k - cum;
+        break;
+      }
+      cum += h;
+    }
+  }
+}
+
+
+// Selection: the block sums locate the reduction block holding each
+// rank, a scan of that block's 256 bins locates the key.  Also assembles
+// the result (16-bit sources: complete; fp32: all but the percentiles).
+__global__ __launch_bounds__(kRedThreads) void calib_select_kernel(CalibParams p) {
+  __shared__ unsigned long long s_tmp[kRedThreads / kWave];
+  __shared__ unsigned long long s_pick[4];
+  __shared__ unsigned long long s_red[kRedThreads / kWave][8];
+  if (threadIdx.x < 4) s_pick[threadIdx.x] = 0ull;
+  const Ws w = ws_of(p);
+  const int t = threadIdx.x;
+  unsigned long long c[8];
+#pragma unroll
+  for (int f = 0; f < 8; ++f) c[f] = t < kRedBlocks ? w.blk[t * 8 + f] : 0ull;
+  const unsigned long long bsum = c[kCntBins];
+  block_reduce6<8>(c, s_red);                       // c = totals, m = c[kCntBins]
+  const unsigned long long m = c[kCntBins];
+  unsigned long long tot;
+  const unsigned long long bexcl = block_exscan(bsum, s_tmp, tot);
+  const unsigned long long k[2] = {(999ull * m + 999ull) / 1000ull,      // ceil(999 m / 1000)
+                                   (9999ull * m + 9999ull) / 10000ull};  // ceil(9999 m / 10000)
+  for (int q = 0; q < 2; ++q) {
+    __shared__ unsigned long long s_blk[2];
+    if (t < kRedBlocks && m > 0 && k[q] > bexcl && k[q] <= bexcl + bsum) {
+      s_blk[0] = t;
+      s_blk[1] = bexcl;
+    }
+    __syncthreads();
+    if (m > 0) {
+      const unsigned long long blk = s_blk[0];
+      const unsigned long long h = w.hist1[blk * kRedThreads + t];
+      unsigned long long all;
+      const unsigned long long ex = s_blk[1] + block_exscan(h, s_tmp, all);
+      if (k[q] > ex && k[q] <= ex + h) {
+        s_pick[2 * q] = blk * kRedThreads + t;
+        s_pick[2 * q + 1] = k[q] - ex;
+      }
+    }
+    __syncthreads();
+  }
+  if (t == 0) {
+    const bool k16 = p.src_dtype != kDtFP32;
+    qkv_calib_result r;
+    r.count = (uint64_t)p.n;
+    r.nan = c[kCntNan];
+    r.nonzero = c[kCntNonzero];
+    r.saturated = c[kCntSat];
+    r.below_min_subnormal = c[kCntBelow];
+    r.subnormal = c[kCntSub];
+    r.max_abs = m > 0 ? __uint_as_float((uint32_t)c[kCntAmax]) : 0.f;
+    r.p999 = 0.f;
+    r.p9999 = 0.f;
+    r.reserved = 0u;
+    if (m > 0 && k16) {
+      r.p999 = __uint_as_float(key_bits(p.src_dtype, (uint32_t)s_pick[0]));
+      r.p9999 = __uint_as_float(key_bits(p.src_dtype, (uint32_t)s_pick[2]));
+    }
+    *p.out = r;
+    w.sel[kSelValid] = m > 0;
+    w.sel[kSelB1] = s_pick[0];
+    w.sel[kSelR1] = s_pick[1];
+    w.sel[kSelB2] = s_pick[2];
+    w.sel[kSelR2] = s_pick[3];
+  }
+}
+
+// fp32 sources: low 16 magnitude bits of the elements in the selected bins
+__global__ __launch_bounds__(256) void calib_pass2_kernel(CalibParams p) {
+  const Ws w = ws_of(p);
+  if (!w.sel[kSelValid]) return;
+  const uint32_t b1 = (uint32_t)w.sel[kSelB1], b2 = (uint32_t)w.sel[kSelB2];
+  const uint32_t* x = static_cast<const uint32_t*>(p.x);
+  const int64_t nvec = p.n / 4;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < nvec; v += stride) {
+    const u32x4 a = reinterpret_cast<const u32x4*>(x)[v];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t ab = a[k] & 0x7FFFFFFFu;
+      if (ab > 0x7F800000u) continue;
+      const uint32_t key = ab >> 16;
+      if (key == b1) atomicAdd(&w.hist2[ab & 0xFFFFu], 1ull);
+      if (key == b2) atomicAdd(&w.hist2[kLowBins + (ab & 0xFFFFu)], 1ull);
+    }
+  }
+  if (blockIdx.x == 0 && threadIdx.x < p.n - nvec * 4) {
+    const uint32_t ab = x[nvec * 4 + threadIdx.x] & 0x7FFFFFFFu;
+    if (ab <= 0x7F800000u) {
+      const uint32_t key = ab >> 16;
+      if (key == b1) atomicAdd(&w.hist2[ab & 0xFFFFu], 1ull);
+      if (key == b2) atomicAdd(&w.hist2[kLowBins + (ab & 0xFFFFu)], 1ull);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kSelThreads) void calib_select2_kernel(CalibParams p) {
+  __shared__ unsigned long long s_tmp[kSelThreads / kWave];
+  __shared__ unsigned long long s_pick[4];
+  const Ws w = ws_of(p);
+  if (!w.sel[kSelValid]) return;
+  constexpr int kPer = kLowBins / kSelThreads;
+  for (int t = 0; t < 2; ++t) {
+    const unsigned long long* h = w.hist2 + t * kLowBins;
+    unsigned long long mine = 0;
+    for (int i = 0; i < kPer; ++i) mine += h[threadIdx.x * kPer + i];
+    unsigned long long tot;
+    const unsigned long long excl = block_exscan(mine, s_tmp, tot);
+    find_rank(h, kPer, excl, w.sel[t ? kSelR2 : kSelR1], s_pick + 2 * t);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    p.out->p999 = __uint_as_float(((uint32_t)w.sel[kSelB1] << 16) | (uint32_t)s_pick[0]);
+    p.out->p9999 = __uint_as_float(((uint32_t)w.sel[kSelB2] << 16) | (uint32_t)s_pick[2]);
+  }
+}
+
+template <int SRC>
+hipError_t launch_src(const CalibParams& p, unsigned grid, hipStream_t s) {
+  calib_pass1_kernel<SRC><<<grid, dim3(kPassThreads), 0, s>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t calib_workspace_bytes() {
+  return (size_t)kHeadWords * 8 + (size_t)kMaxPass1 * kBins * 4;
+}
+
+hipError_t launch_calib(const CalibParams& p, hipStream_t s) {
+  hipError_t e = hipSuccess;
+  if (p.src_dtype == kDtFP32) {
+    calib_clear_kernel<<<64, dim3(256), 0, s>>>(p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // one workgroup per CU (the 128 KB histogram fills a CU's LDS), at most
+  // one per 64K elements
+  const int64_t want = (p.n + 65535) / 65536;
+  CalibParams q = p;
+  q.grid1 = (int)(want < 1 ? 1 : (want > kMaxPass1 ? kMaxPass1 : want));
+  switch (q.src_dtype) {
+    case kDtFP32: e = launch_src<kDtFP32>(q, q.grid1, s); break;
+    case kDtBF16: e = launch_src<kDtBF16>(q, q.grid1, s); break;
+    default: e = launch_src<kDtFP16>(q, q.grid1, s); break;
+  }
+  if (e != hipSuccess) return e;
+  calib_reduce_kernel<<<kRedBlocks, dim3(kRedThreads), 0, s>>>(q);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  calib_select_kernel<<<1, dim3(kRedThreads), 0, s>>>(q);
+  e = hipGetLastError();
+  if (e != hipSuccess || q.src_dtype != kDtFP32) return e;
+  const int64_t want2 = (q.n / 4 + 255) / 256;
+  const unsigned grid2 = (unsigned)(want2 < 1 ? 1 : (want2 > 2048 ? 2048 : want2));
+  calib_pass2_kernel<<<grid2, dim3(256), 0, s>>>(q);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  calib_select2_kernel<<<1, dim3(kSelThreads), 0, s>>>(q);
+  return hipGetLastError();
+}
+
+}  // namespace qsakv

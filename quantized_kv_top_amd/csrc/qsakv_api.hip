@@ -35,6 +35,35 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
 
 bool scale_ok(float s) { return std::isfinite(s) && s >= std::numeric_limits<float>::min(); }
 
+// The E4M3 converter's float32 quotient, on the host (IEEE binary32).
+float div_f32(float a, float b) {
+  volatile float q = a / b;
+  return q;
+}
+
+// Smallest non-negative float32 bit pattern u (as |x|) whose quotient
+// y = fl32(|x| / scale) satisfies the predicate; y is non-decreasing in u
+// (division by a positive number and round-to-nearest are monotone), and
+// u = +inf satisfies every predicate, so a binary search is exact.
+enum CalibPred { kCalibSat, kCalibSub, kCalibNorm };
+uint32_t calib_threshold(float scale, CalibPred pred) {
+  uint32_t lo = 0, hi = 0x7F800000u;
+  while (lo < hi) {
+    const uint32_t mid = lo + (hi - lo) / 2;
+    float v;
+    std::memcpy(&v, &mid, 4);
+    const float y = div_f32(v, scale);
+    const bool ok = pred == kCalibSat ? y > 448.0f
+                    : pred == kCalibSub ? y >= 0x1p-9f
+                                        : y >= 0x1p-6f;
+    if (ok)
+      hi = mid;
+    else
+      lo = mid + 1;
+  }
+  return lo;
+}
+
 int64_t row_bytes(int kind, int64_t d) {
   switch (kind) {
     case QKV_CACHE_INT8: return d;
@@ -229,6 +258,30 @@ qkv_status qsa_sparse_attn_decode(const qkv_cache* cache, const qsa_args* args, 
   const hipError_t e = qsakv::launch_attn(cache->kind, cache->head_dim, p, s);
   if (e != hipSuccess) return finish(e);
   return finish(qsakv::launch_merge(cache->head_dim, p, s));
+}
+
+size_t qkv_calib_workspace_bytes(void) { return qsakv::calib_workspace_bytes(); }
+
+qkv_status kv_calib_stats(const void* x, int32_t src_dtype, int64_t n, float scale,
+                          qkv_calib_result* out, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (src_dtype < QKV_BF16 || src_dtype > QKV_FP32) return QKV_ERR_UNSUPPORTED;
+  if (n < 0) return QKV_ERR_BAD_SHAPE;
+  if (!out || (n > 0 && !x)) return QKV_ERR_NULL;
+  if (!scale_ok(scale)) return QKV_ERR_BAD_SCALE;
+  if (!aligned(out, 8) || (x && !aligned(x, 16))) return QKV_ERR_ALIGNMENT;
+  if (!workspace || workspace_bytes < qsakv::calib_workspace_bytes() || !aligned(workspace, 256))
+    return QKV_ERR_WORKSPACE;
+  qsakv::CalibParams p;
+  p.x = x;
+  p.n = n;
+  p.src_dtype = src_dtype;
+  p.t_sat = calib_threshold(scale, kCalibSat);
+  p.t_sub = calib_threshold(scale, kCalibSub);
+  p.t_norm = calib_threshold(scale, kCalibNorm);
+  p.workspace = workspace;
+  p.out = out;
+  return finish(qsakv::launch_calib(p, static_cast<hipStream_t>(stream)));
 }
 
 qkv_status qkv_cache_bytes(int32_t kind, int32_t num_blocks, int32_t block_size,

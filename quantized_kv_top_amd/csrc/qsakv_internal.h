@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "qsakv.h"
+
 namespace qsakv {
 
 enum Kind : int { kInt8 = 0, kInt8Inline = 1, kE4M3 = 2, kBF16 = 3 };
@@ -26,6 +28,22 @@ struct WriteParams {
 };
 
 hipError_t launch_kv_write(int kind, int head_dim, const WriteParams& p, hipStream_t s);
+
+// Calibration statistics of one tensor; thresholds are float32 bit patterns
+// of |x| (the smallest |x| whose quotient by the scale is > 448, >= 2^-9,
+// >= 2^-6), derived on the host.
+struct CalibParams {
+  const void* x;
+  int64_t n;
+  int32_t src_dtype;
+  uint32_t t_sat, t_sub, t_norm;
+  void* workspace;
+  qkv_calib_result* out;
+  int32_t grid1;          // streaming workgroups (set by the launcher)
+};
+
+size_t calib_workspace_bytes();
+hipError_t launch_calib(const CalibParams& p, hipStream_t s);
 
 // Everything an attention kernel needs; validated by the caller.
 struct AttnParams {

@@ -24,8 +24,8 @@ KIND_BY_NAME = {"int8": CACHE_INT8, "int8_inline": CACHE_INT8_INLINE,
                 "e4m3": CACHE_E4M3, "bf16": CACHE_BF16}
 
 EXPORTED = ("kv_quant_write", "qsa_sparse_attn_prefill", "qsa_decode_workspace_bytes",
-            "qsa_sparse_attn_decode", "qkv_cache_bytes", "qkv_status_str",
-            "qkv_last_hip_error", "qkv_abi_version")
+            "qsa_sparse_attn_decode", "qkv_calib_workspace_bytes", "kv_calib_stats",
+            "qkv_cache_bytes", "qkv_status_str", "qkv_last_hip_error", "qkv_abi_version")
 
 
 class QkvCache(ctypes.Structure):
@@ -45,6 +45,14 @@ class QsaArgs(ctypes.Structure):
                 ("topk", ctypes.c_int32), ("topk_idx", ctypes.c_void_p),
                 ("sm_scale", ctypes.c_float), ("out_dtype", ctypes.c_int32),
                 ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p)]
+
+
+class QkvCalibResult(ctypes.Structure):
+    _fields_ = [("count", ctypes.c_uint64), ("nan", ctypes.c_uint64),
+                ("nonzero", ctypes.c_uint64), ("saturated", ctypes.c_uint64),
+                ("below_min_subnormal", ctypes.c_uint64), ("subnormal", ctypes.c_uint64),
+                ("max_abs", ctypes.c_float), ("p999", ctypes.c_float),
+                ("p9999", ctypes.c_float), ("reserved", ctypes.c_uint32)]
 
 
 _lib = None
@@ -69,6 +77,10 @@ def lib():
     L.qsa_decode_workspace_bytes.restype = c_sz
     L.qsa_sparse_attn_decode.argtypes = [P(QkvCache), P(QsaArgs), c_i32, c_vp, c_sz, c_vp]
     L.qsa_sparse_attn_decode.restype = c_i32
+    L.qkv_calib_workspace_bytes.argtypes = []
+    L.qkv_calib_workspace_bytes.restype = c_sz
+    L.kv_calib_stats.argtypes = [c_vp, c_i32, c_i64, ctypes.c_float, c_vp, c_vp, c_sz, c_vp]
+    L.kv_calib_stats.restype = c_i32
     L.qkv_cache_bytes.argtypes = [c_i32, c_i32, c_i32, c_i32, c_i32, P(c_sz), P(c_sz), P(c_sz)]
     L.qkv_cache_bytes.restype = c_i32
     L.qkv_status_str.argtypes = [c_i32]
@@ -198,3 +210,24 @@ def qsa_sparse_attn_decode(cache, q, row_seq, block_table, topk_idx, sm_scale, o
     wb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().qsa_sparse_attn_decode(ctypes.byref(d), ctypes.byref(a), num_splits, wp, wb,
                                         _stream(stream)), "qsa_sparse_attn_decode")
+
+
+def calib_workspace_bytes():
+    return int(lib().qkv_calib_workspace_bytes())
+
+
+def kv_calib_stats(x, scale, out, workspace, stream=None):
+    """Calibration statistics of the device tensor ``x`` (fp16 / bf16 / fp32,
+    contiguous) at the E4M3 ``scale``, written by the library into ``out``
+    (a device uint8 tensor of at least sizeof(qkv_calib_result) bytes)."""
+    assert x.is_contiguous() and out.numel() >= ctypes.sizeof(QkvCalibResult)
+    _check(lib().kv_calib_stats(_ptr(x), dtype_code(x), x.numel(), float(scale), _ptr(out),
+                                _ptr(workspace), workspace.numel(), _stream(stream)),
+           "kv_calib_stats")
+
+
+def calib_result(out):
+    """Read a qkv_calib_result from ``out`` (device or host uint8 tensor)."""
+    raw = bytes(out[:ctypes.sizeof(QkvCalibResult)].cpu().numpy().tobytes())
+    r = QkvCalibResult.from_buffer_copy(raw)
+    return {k: getattr(r, k) for k, _ in QkvCalibResult._fields_ if k != "reserved"}

@@ -159,3 +159,32 @@ def test_status_strings():
     for s in range(8):
         assert L.qkv_status_str(s).decode().startswith("QKV_")
     assert b"unknown" in L.qkv_status_str(99)
+
+
+def _calib(x=DUMMY, dt=qsakv.FP16, n=1000, scale=1.0, out=DUMMY, ws=DUMMY, wsb=None):
+    L = qsakv.lib()
+    wsb = L.qkv_calib_workspace_bytes() if wsb is None else wsb
+    return L.kv_calib_stats(x, dt, n, scale, out, ws, wsb, None)
+
+
+def test_calib_struct_and_validation():
+    """qkv_calib_result layout, and every rejection happens before a launch."""
+    assert ctypes.sizeof(qsakv.QkvCalibResult) == 64
+    assert qsakv.QkvCalibResult.max_abs.offset == 48
+    L = qsakv.lib()
+    # uint64: a 32K-bin and two 64K-bin histograms, selection state, 256
+    # per-workgroup and 128 per-reduction-block counter sets; then 256
+    # uint32 32K-bin per-workgroup histograms
+    assert L.qkv_calib_workspace_bytes() == (32768 + 2 * 65536 + 8 + 256 * 8 + 128 * 8) * 8 \
+        + 256 * 32768 * 4
+    assert _calib(dt=3) == qsakv.ERR_UNSUPPORTED
+    assert _calib(n=-1) == qsakv.ERR_BAD_SHAPE
+    assert _calib(x=None) == qsakv.ERR_NULL
+    assert _calib(out=None) == qsakv.ERR_NULL
+    for s in [float("nan"), float("inf"), 0.0, -1.0, 1e-40]:
+        assert _calib(scale=s) == qsakv.ERR_BAD_SCALE
+    assert _calib(x=DUMMY + 8) == qsakv.ERR_ALIGNMENT
+    assert _calib(out=DUMMY + 4) == qsakv.ERR_ALIGNMENT
+    assert _calib(ws=None) == qsakv.ERR_WORKSPACE
+    assert _calib(ws=DUMMY + 128) == qsakv.ERR_WORKSPACE
+    assert _calib(wsb=L.qkv_calib_workspace_bytes() - 1) == qsakv.ERR_WORKSPACE
