@@ -40,10 +40,15 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# the sources the attention kernels are built from (their launch parameters
+# included): a change to any of them invalidates the committed counters
+ATTN_SOURCES = ("attn.hip", "qsakv_device.h", "qsakv_internal.h", "qsakv_api.hip")
+
+
 def source_sha():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "quantized_kv_top_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in ATTN_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -135,8 +140,9 @@ class PrefillLayer:
 
 
 def cpu_baseline_prefill(seed, budget_s, rows_cap):
-    """The oracle, as it stands, on the first rows of one prefill layer."""
-    from threadpoolctl import threadpool_info
+    """The oracle, as it stands, on the first rows of one prefill layer: with
+    all BLAS threads (the reported value) and again on one thread."""
+    from threadpoolctl import threadpool_info, threadpool_limits
     from oracle import attention as oatt
     from oracle import cache as ocache
 
@@ -146,18 +152,29 @@ def cpu_baseline_prefill(seed, budget_s, rows_cap):
     oc.write(wl.to_numpy_src(w.k_src), wl.to_numpy_src(w.v_src), "bf16", w.slot_mapping)
     write_s = time.perf_counter() - t0
     qn = wl.to_numpy_src(w.q)
-    done = 0
-    t0 = time.perf_counter()
-    while done < rows_cap and time.perf_counter() - t0 < budget_s:
-        oatt.sparse_attention(oc, qn, "bf16", w.row_seq, w.block_table, w.topk_idx,
-                              w.sm_scale, rows=[done % w.num_rows])
-        done += 1
-    el = time.perf_counter() - t0
+
+    def rate(budget):
+        done = 0
+        t0 = time.perf_counter()
+        while done < rows_cap and time.perf_counter() - t0 < budget:
+            oatt.sparse_attention(oc, qn, "bf16", w.row_seq, w.block_table, w.topk_idx,
+                                  w.sm_scale, rows=[done % w.num_rows])
+            done += 1
+        return done, time.perf_counter() - t0
+
+    done, el = rate(budget_s)
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    with threadpool_limits(limits=1):
+        done1, el1 = rate(budget_s / 3)
+    per_row = gathered_bytes_per_row("int8", w.topk, w.num_kv_heads, w.head_dim)
     return {"value": done / el, "unit": "rows/s", "cores": threads, "kind": "oracle",
             "sample": "%d prefill rows (rows 0.. of %d, cycled; top-k %d, fp64 numpy) in "
-                      "%.1f s; oracle quantize-on-write of all %d tokens took %.1f s"
-                      % (done, w.num_rows, w.topk, el, w.slot_mapping.size, write_s)}
+                      "%.1f s with %d BLAS threads; oracle quantize-on-write of all %d tokens "
+                      "took %.1f s" % (done, w.num_rows, w.topk, el, threads,
+                                       w.slot_mapping.size, write_s),
+            "gathered_GBps": done / el * per_row / 1e9,
+            "one_thread_rows_per_s": done1 / el1,
+            "one_thread_gathered_GBps": done1 / el1 * per_row / 1e9}
 
 
 def bench_prefill(args):
