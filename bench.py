@@ -199,7 +199,7 @@ def bench_prefill(args):
     bytes_launch = rows * gathered_bytes_per_row("int8", topk, 2, 256)
     kern_ms = float(np.mean(per))
     achieved = bytes_launch / (kern_ms / 1e3) / 1e9
-    traffic = traffic_from_profile("qsa_attn16_kernel<int8,256>", "prefill")
+    traffic = traffic_from_profile("qsa_attn16_kernel<int8,256,4>", "prefill")
     inl_ms = res["int8_inline"][0] / args.steps
     line = {
         "metric": METRIC, "value": value, "unit": "rows/s", "n_gpus": 1,
@@ -217,7 +217,7 @@ def bench_prefill(args):
                    "inline260_over_aligned": inl_ms / ms},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel": "qsa_attn16_kernel<int8,256>",
+                     "kernel": "qsa_attn16_kernel<int8,256,4>",
                      "kernel_ms": kern_ms},
     }
     if not args.no_cpu_baseline:
