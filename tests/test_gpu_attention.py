@@ -320,3 +320,50 @@ def test_decode_workspace_reuse():
         torch.cuda.synchronize()
         check(out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
               ro[:rows], rl[:rows], "reuse rows %d" % rows)
+
+
+def test_graph_replays_match_eager():
+    """Write, prefill, split-K decode and calibration statistics captured in
+    one HIP graph: every replay (with eager work and synchronizations in
+    between) reproduces the eager results bit for bit."""
+    w = small_workload(seed=41, topk=200, rows=10)
+    c = qsakv.Cache("int8", w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, "cuda")
+    ks, vs = w.k_src.cuda(), w.v_src.cuda()
+    sm = dev(w.slot_mapping, torch.int64)
+    q = w.q.cuda().contiguous()
+    rs, bt, idx = dev(w.row_seq, torch.int32), dev(w.block_table, torch.int32), \
+        dev(w.topk_idx, torch.int32)
+    R, Hq, D = q.shape
+    out1 = torch.empty((R, Hq, D), dtype=torch.bfloat16, device="cuda")
+    out2 = torch.empty_like(out1)
+    lse = torch.empty((R, Hq), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(qsakv.qsa_decode_workspace_bytes(R, Hq, D, 8), dtype=torch.uint8,
+                     device="cuda")
+    cres = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    cws = torch.zeros(qsakv.calib_workspace_bytes(), dtype=torch.uint8, device="cuda")
+    xs = ks.reshape(-1)
+
+    def step(stream):
+        qsakv.kv_quant_write(c, ks, vs, sm, stream=stream)
+        qsakv.qsa_sparse_attn_prefill(c, q, rs, bt, idx, w.sm_scale, out1, lse=lse,
+                                      stream=stream)
+        qsakv.qsa_sparse_attn_decode(c, q, rs, bt, idx, w.sm_scale, out2, 8, ws, stream=stream)
+        qsakv.kv_calib_stats(xs, 0.05, cres, cws, stream=stream)
+
+    step(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (c.k, c.kv_scale, out1, lse, out2, cres)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step(s)
+    for i in range(3):
+        for t in (c.k, c.kv_scale, out1, lse, out2, cres, ws, cws):
+            t.zero_()                    # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        say("graph replay", i)
+        for a, b in zip((c.k, c.kv_scale, out1, lse, out2, cres), ref):
+            assert torch.equal(a, b)
