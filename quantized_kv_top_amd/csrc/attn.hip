@@ -14,7 +14,7 @@
 //   One workgroup (4 waves) per (row, KV head, split partition).  The
 //   workgroup first resolves the partition's positions to slots (index ->
 //   block table -> slot) into LDS, then its waves take the partition's
-//   tiles of TT tokens round-robin, keeping kDepth tiles of gathered rows in
+//   tiles of 16 tokens round-robin, keeping kDepth tiles of gathered rows in
 //   registers: kDepth - 1 in flight while one is computed.  Waves merge in
 //   LDS in a fixed order (bitwise reproducible).  With several partitions,
 //   each writes an unnormalized partial and a second, small launch merges
@@ -25,8 +25,8 @@
 //   online softmax over the tile (log2 domain, running max per head)
 //   O^T[d][h] += V^T[d][t] . W[t][h]       A = V^T (M = 16 d's), B = W
 // so the G query heads share every gathered K/V tile.  The QK^T output of a
-// 16-token block gives each lane 4 tokens of one head, which is exactly the
-// B operand of a K = 16 MFMA (TT = 16) or half of a K = 32 one (TT = 32).
+// 16-token tile gives each lane 4 tokens of one head, which is exactly the
+// B operand of the K = 16 PV MFMA.
 //
 // Exact operands.  E4M3 codes become fp16 through gfx950's OCP-FP8 convert.
 // An int8 code q becomes the fp16 value 1152 + q (0x64 in the high byte and
@@ -34,7 +34,8 @@
 // 1152 is removed after the MFMA: from each logit as 1152 * sum_d q'_d, and
 // from the output as 1152 * sum_t W_t, both sums of exactly what entered the
 // MFMA.  Queries are rounded to fp16 after an exact power-of-two prescale;
-// bf16 caches run bf16 MFMA directly.
+// bf16 caches run bf16 MFMA directly (their query operand staged in LDS at
+// D = 256, where the registers go to the tiles in flight).
 //
 // Scales.  The int8 per-token K scale multiplies the logit after the dot
 // product; the per-token V scale enters the softmax weight
@@ -59,6 +60,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 template <int KIND, int D, int TT>
 struct Geo {
+  static_assert(TT == 16, "tiles are 16 tokens: one MFMA block of K rows");
   static constexpr bool kOneByte = KIND != kBF16;
   static constexpr bool kInt = KIND == kInt8 || KIND == kInt8Inline;
   static constexpr int kDataBytes = kOneByte ? D : 2 * D;              // K or V row payload
@@ -70,10 +72,12 @@ struct Geo {
   static constexpr int kPV = D / 16;                                    // PV MFMAs per tile
   static constexpr int kOut = D / 4;                                    // outputs per lane
   static constexpr int kBlk = TT / 16;                                  // 16-token blocks
+  // bf16 at D = 256: the query operand (32 registers) lives in LDS so that
+  // 16-token tiles fit two waves per SIMD
+  static constexpr bool kQLds = KIND == kBF16 && D == 256;
   static constexpr int kTok = TT / 4;                                   // V tokens per lane
-  // tiles held in registers per wave: three where they fit next to the
-  // accumulators, else two
-  static constexpr int kDepth = (TT == 32 && kOneByte && D == 256) ? 3 : 2;
+  // tiles held in registers per wave: one in flight while one is computed
+  static constexpr int kDepth = 2;
 };
 
 // Raw gathered data of one tile, as held by one lane.
@@ -119,10 +123,6 @@ __device__ __forceinline__ void issue_tile(TileRaw<KIND, D, TT>& t, const AttnPa
   {
     const int4 s0 = *reinterpret_cast<const int4*>(ts + 4 * grp);
     vs[0] = s0.x; vs[1] = s0.y; vs[2] = s0.z; vs[3] = s0.w;
-    if constexpr (G::kTok == 8) {
-      const int4 s1 = *reinterpret_cast<const int4*>(ts + 16 + 4 * grp);
-      vs[4] = s1.x; vs[5] = s1.y; vs[6] = s1.z; vs[7] = s1.w;
-    }
   }
   uint32_t valid = 0;
 #pragma unroll
@@ -180,6 +180,20 @@ struct WaveState {
 template <int KIND>
 using QOp = std::conditional_t<KIND == kBF16, bf16x8, f16x8>;
 
+// Where a tile reads the query operand (B of QK^T) from: the wave's
+// registers, or -- where the registers are needed for the tiles in flight
+// -- the workgroup's copy in LDS.
+template <int KIND, int N>
+struct QRegs {
+  QOp<KIND> v[N];
+  __device__ __forceinline__ QOp<KIND> operator[](int i) const { return v[i]; }
+};
+template <int KIND>
+struct QLds {
+  const QOp<KIND>* p;   // this lane's first vector; vectors are kWave apart
+  __device__ __forceinline__ QOp<KIND> operator[](int i) const { return p[i * kWave]; }
+};
+
 // Byte lanes of the token pair (x, y) interleaved: tk[0] = (x0 y0 x1 y1),
 // tk[1] = (x2 y2 x3 y3); int8 codes are biased to q + 128 on the way.
 template <int KIND>
@@ -201,13 +215,15 @@ __device__ __forceinline__ uint32_t v_pair_f16(const uint32_t (&tk)[2], int bb) 
     return i8pair_to_f16x2(tk[half], hi ? kSelB23 : kSelB01);
 }
 
-template <int KIND, int D, int TT>
-__device__ __forceinline__ void compute_tile(const TileRaw<KIND, D, TT>& t,
-                                             const QOp<KIND> (&q)[Geo<KIND, D, TT>::kQK],
+template <int KIND, int D, int TT, typename QS>
+__device__ __forceinline__ void compute_tile(const TileRaw<KIND, D, TT>& t, const QS& q,
                                              float kfac, float kbias, WaveState& st,
                                              f32x4 (&o)[Geo<KIND, D, TT>::kPV]) {
   using G = Geo<KIND, D, TT>;
   constexpr int NT = G::kTok;
+  // an LDS-resident query is read again for every tile (not kept live in
+  // registers across the loop)
+  if constexpr (G::kQLds) __asm__ volatile("" ::: "memory");
   // ---- S^T = K Q^T for the 16-token blocks -------------------------------
   f32x4 s[G::kBlk];
 #pragma unroll
@@ -303,24 +319,14 @@ __device__ __forceinline__ void compute_tile(const TileRaw<KIND, D, TT>& t,
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
         const uint32_t sel = hb ? 0x07060302u : 0x05040100u;
-        if constexpr (TT == 32) {
-          bf16x8 bw;
+        bf16x4 bw;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) bw[e] = (__bf16)w[e];
-          u32x4 a;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) a[k] = perm(t.v[2 * k + 1][c], t.v[2 * k][c], sel);
-          o[2 * c + hb] = mfma16(bitcast<bf16x8>(a), bw, o[2 * c + hb]);
-        } else {
-          bf16x4 bw;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) bw[e] = (__bf16)w[e];
-          u32x2 a;
-          a[0] = perm(t.v[1][c], t.v[0][c], sel);
-          a[1] = perm(t.v[3][c], t.v[2][c], sel);
-          o[2 * c + hb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bitcast<bf16x4>(a), bw,
-                                                                     o[2 * c + hb], 0, 0, 0);
-        }
+        for (int e = 0; e < 4; ++e) bw[e] = (__bf16)w[e];
+        u32x2 a;
+        a[0] = perm(t.v[1][c], t.v[0][c], sel);
+        a[1] = perm(t.v[3][c], t.v[2][c], sel);
+        o[2 * c + hb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bitcast<bf16x4>(a), bw,
+                                                                   o[2 * c + hb], 0, 0, 0);
       }
     }
   } else {
@@ -331,24 +337,14 @@ __device__ __forceinline__ void compute_tile(const TileRaw<KIND, D, TT>& t,
       for (int k = 0; k < NT / 2; ++k) interleave_pair<KIND>(t.v[2 * k][c], t.v[2 * k + 1][c], tk[k]);
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) {
-        if constexpr (TT == 32) {
-          f16x8 bw;
+        f16x4 bw;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) bw[e] = (_Float16)w[e];
-          u32x4 r;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) r[k] = v_pair_f16<KIND>(tk[k], bb);
-          o[4 * c + bb] = mfma16(bitcast<f16x8>(r), bw, o[4 * c + bb]);
-        } else {
-          f16x4 bw;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) bw[e] = (_Float16)w[e];
-          u32x2 r;
-          r[0] = v_pair_f16<KIND>(tk[0], bb);
-          r[1] = v_pair_f16<KIND>(tk[1], bb);
-          o[4 * c + bb] = __builtin_amdgcn_mfma_f32_16x16x16f16(bitcast<f16x4>(r), bw,
-                                                                 o[4 * c + bb], 0, 0, 0);
-        }
+        for (int e = 0; e < 4; ++e) bw[e] = (_Float16)w[e];
+        u32x2 r;
+        r[0] = v_pair_f16<KIND>(tk[0], bb);
+        r[1] = v_pair_f16<KIND>(tk[1], bb);
+        o[4 * c + bb] = __builtin_amdgcn_mfma_f32_16x16x16f16(bitcast<f16x4>(r), bw,
+                                                               o[4 * c + bb], 0, 0, 0);
       }
     }
   }
@@ -393,6 +389,7 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
   __shared__ __align__(16) int s_slot[kChunk];
   __shared__ float s_m[NW][16], s_l[NW][16];
   __shared__ f32x4 s_obuf[NW / 2][G::kPV * kWave];
+  __shared__ QOp<KIND> s_q[G::kQLds ? G::kQK * kWave : 1];
 
   const int lane = lane_id(), ln16 = lane & 15, grp = lane >> 4;
   const int w = threadIdx.x >> 6;
@@ -520,6 +517,19 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
     }
   }
 
+  using QS = std::conditional_t<G::kQLds, QLds<KIND>, QRegs<KIND, G::kQK>>;
+  QS qs;
+  if constexpr (G::kQLds) {
+    if (w == 0) {          // published by the barrier ahead of the first tile
+#pragma unroll
+      for (int i = 0; i < G::kQK; ++i) s_q[i * kWave + lane] = qop[i];
+    }
+    qs.p = s_q + lane;
+  } else {
+#pragma unroll
+    for (int i = 0; i < G::kQK; ++i) qs.v[i] = qop[i];
+  }
+
   // ---- the wave's tiles -----------------------------------------------------
   WaveState st{kNegInf, 0.f, 0.f, 0.f, 0.f};
   f32x4 o[G::kPV];
@@ -538,31 +548,15 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
     // tiles w, w + NW, w + 2 NW, ... of the chunk, kDepth of them in
     // registers: kDepth - 1 in flight while one is computed
     auto ts = [&](int k) { return s_slot + (w + NW * k) * TT; };
-    TileRaw<KIND, D, TT> ta, tb, tc;
+    TileRaw<KIND, D, TT> ta, tb;
     if (my_n > 0) issue_tile<KIND, D, TT>(ta, p, g, ts(0));
     if (my_n > 1) issue_tile<KIND, D, TT>(tb, p, g, ts(1));
-    if constexpr (G::kDepth == 3) {
-      if (my_n > 2) issue_tile<KIND, D, TT>(tc, p, g, ts(2));
-      for (int k = 0; k < my_n; k += 3) {
-        compute_tile<KIND, D, TT>(ta, qop, kfac, kbias, st, o);
-        if (k + 3 < my_n) issue_tile<KIND, D, TT>(ta, p, g, ts(k + 3));
-        if (k + 1 < my_n) {
-          compute_tile<KIND, D, TT>(tb, qop, kfac, kbias, st, o);
-          if (k + 4 < my_n) issue_tile<KIND, D, TT>(tb, p, g, ts(k + 4));
-        }
-        if (k + 2 < my_n) {
-          compute_tile<KIND, D, TT>(tc, qop, kfac, kbias, st, o);
-          if (k + 5 < my_n) issue_tile<KIND, D, TT>(tc, p, g, ts(k + 5));
-        }
-      }
-    } else {
-      for (int k = 0; k < my_n; k += 2) {
-        compute_tile<KIND, D, TT>(ta, qop, kfac, kbias, st, o);
-        if (k + 2 < my_n) issue_tile<KIND, D, TT>(ta, p, g, ts(k + 2));
-        if (k + 1 < my_n) {
-          compute_tile<KIND, D, TT>(tb, qop, kfac, kbias, st, o);
-          if (k + 3 < my_n) issue_tile<KIND, D, TT>(tb, p, g, ts(k + 3));
-        }
+    for (int k = 0; k < my_n; k += 2) {
+      compute_tile<KIND, D, TT, QS>(ta, qs, kfac, kbias, st, o);
+      if (k + 2 < my_n) issue_tile<KIND, D, TT>(ta, p, g, ts(k + 2));
+      if (k + 1 < my_n) {
+        compute_tile<KIND, D, TT, QS>(tb, qs, kfac, kbias, st, o);
+        if (k + 3 < my_n) issue_tile<KIND, D, TT>(tb, p, g, ts(k + 3));
       }
     }
   }
@@ -643,16 +637,11 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
   }
 }
 
-// 16-token tiles ask for two waves per SIMD (<= 256 registers per wave);
-// 32-token tiles keep more rows in flight per wave at one wave per SIMD.
+// 16-token tiles at two waves per SIMD (<= 256 registers per wave).
 template <int KIND, int D, int NW>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void qsa_attn16_kernel(AttnParams p) {
   attn_body<KIND, D, 16, NW>(p);
-}
-template <int KIND, int D, int NW>
-__global__ __launch_bounds__(NW * kWave) void qsa_attn32_kernel(AttnParams p) {
-  attn_body<KIND, D, 32, NW>(p);
 }
 
 // Log-sum-exp merge of the split-K partials of one (row, head) per wave:
@@ -726,19 +715,6 @@ __global__ __launch_bounds__(kWave) void qsa_merge_kernel(AttnParams p) {
   }
 }
 
-// Tokens per tile.  16 keeps every (kind, D) within 256 registers at two
-// waves per SIMD, except bf16 at D = 256, whose 32-byte-per-element tiles
-// would spill there; it takes 32-token tiles at one wave per SIMD instead.
-// A tuning build may force one size with -DQSAKV_TILE=16|32.
-template <int KIND, int D>
-constexpr int tile_tokens() {
-#ifdef QSAKV_TILE
-  return QSAKV_TILE;
-#else
-  return (KIND == kBF16 && D == 256) ? 32 : 16;
-#endif
-}
-
 // Waves per workgroup.  A workgroup's fixed cost is a chain of dependent
 // memory round trips (list positions, block table, first tile, partial
 // store), so launches with few items spread each item over more waves and
@@ -746,10 +722,7 @@ constexpr int tile_tokens() {
 // chip holds 2048 waves.  Large launches (prefill) keep 4 waves per item.
 template <int KIND, int D, int NW>
 hipError_t launch_knw(const AttnParams& p, unsigned grid, hipStream_t s) {
-  if constexpr (tile_tokens<KIND, D>() == 16)
-    qsa_attn16_kernel<KIND, D, NW><<<grid, dim3(NW * kWave), 0, s>>>(p);
-  else
-    qsa_attn32_kernel<KIND, D, NW><<<grid, dim3(NW * kWave), 0, s>>>(p);
+  qsa_attn16_kernel<KIND, D, NW><<<grid, dim3(NW * kWave), 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -757,12 +730,8 @@ template <int KIND, int D>
 hipError_t launch_kd(const AttnParams& p, hipStream_t s) {
   const int64_t items = (int64_t)p.num_rows * p.num_kv_heads * p.num_splits;
   const unsigned grid = (unsigned)items;
-  if constexpr (tile_tokens<KIND, D>() == 16) {   // two waves per SIMD
-    if (items <= 256) return launch_knw<KIND, D, 8>(p, grid, s);
-    if (items > 512 && items <= 1024) return launch_knw<KIND, D, 2>(p, grid, s);
-  } else {                                         // one wave per SIMD
-    if (items > 256 && items <= 512) return launch_knw<KIND, D, 2>(p, grid, s);
-  }
+  if (items <= 256) return launch_knw<KIND, D, 8>(p, grid, s);
+  if (items > 512 && items <= 1024) return launch_knw<KIND, D, 2>(p, grid, s);
   return launch_knw<KIND, D, 4>(p, grid, s);
 }
 
