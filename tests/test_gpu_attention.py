@@ -367,3 +367,40 @@ def test_graph_replays_match_eager():
         say("graph replay", i)
         for a, b in zip((c.k, c.kv_scale, out1, lse, out2, cres), ref):
             assert torch.equal(a, b)
+
+
+def _random_case(seed):
+    """A seeded random configuration: block size 1..1024, G 1..16, D 128 or
+    256, cache kind, query / output dtypes, list length (up to several LDS
+    chunks of 1024 positions, with padding and duplicates), split count."""
+    rng = np.random.default_rng(seed)
+    kind = KINDS[rng.integers(len(KINDS))]
+    D = int(rng.choice([128, 256]))
+    BS = int(2 ** rng.integers(0, 11))
+    G = int(rng.choice([1, 2, 3, 4, 8, 16]))
+    Hkv = int(rng.integers(1, 4))
+    ctx = int(rng.integers(64, 3000))
+    topk = int(rng.integers(1, min(ctx, 2600) + 1))
+    rows = int(rng.integers(1, 7))
+    q_dtype = "bf16" if kind == "bf16" else str(rng.choice(["bf16", "fp16"]))
+    src = "fp16" if q_dtype == "fp16" else "bf16"
+    w = small_workload(seed=seed, Hq=G * Hkv, Hkv=Hkv, D=D, BS=BS, ctx=ctx, rows=rows,
+                       topk=topk, q_dtype=q_dtype, src=src, pad=int(rng.integers(0, 5)))
+    idx = w.topk_idx.copy()
+    if topk > 2:                         # a duplicated position in some rows
+        idx[0, 1] = idx[0, 0]
+    w.topk_idx = idx
+    P = int(rng.choice([1, 1, 2, 5, 8, 33]))
+    od = str(rng.choice(["fp32", "bf16", "fp16"]))
+    return kind, w, P, od
+
+
+@pytest.mark.parametrize("seed", list(range(100, 124)))
+def test_random_configurations(seed):
+    kind, w, P, od = _random_case(seed)
+    say("random", seed, kind, "D", w.head_dim, "BS", w.block_size, "G",
+        w.num_q_heads // w.num_kv_heads, "Hkv", w.num_kv_heads, "topk", w.topk, "P", P, od)
+    c, oc = _setup(kind, w)
+    ro, rl = oracle_attention(oc, w)
+    o, l = run_attention(c, w, num_splits=P, out_dtype=od, decode=P > 1)
+    check(o, l, ro, rl, "random seed %d" % seed)
