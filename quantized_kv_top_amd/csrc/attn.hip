@@ -49,7 +49,10 @@
 namespace qsakv {
 namespace {
 
-constexpr int kChunk = 1024;          // list positions resolved per LDS batch
+// list positions each thread resolves per LDS batch: 1024 per batch, at
+// most 4 per thread (more would cost registers at one wave per workgroup)
+template <int NW>
+constexpr int pos_per_thread() { return 1024 / (NW * 64) < 4 ? 1024 / (NW * 64) : 4; }
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kMaxSlack = 8.f;      // log2 units the running max may lag behind
 constexpr float kSigSlack = 16.f;     // factor sigma may lag behind a tile's V scale
@@ -385,10 +388,11 @@ template <int KIND, int D, int TT, int NW>
 __device__ __forceinline__ void attn_body(const AttnParams& p) {
   using G = Geo<KIND, D, TT>;
   constexpr int kThreads = NW * kWave;
-  constexpr int kPer = kChunk / kThreads;   // positions resolved per thread and chunk
+  constexpr int kPer = pos_per_thread<NW>();
+  constexpr int kChunk = kPer * kThreads;   // list positions resolved per LDS batch
   __shared__ __align__(16) int s_slot[kChunk];
   __shared__ float s_m[NW][16], s_l[NW][16];
-  __shared__ f32x4 s_obuf[NW / 2][G::kPV * kWave];
+  __shared__ f32x4 s_obuf[NW > 1 ? NW / 2 : 1][G::kPV * kWave];
   __shared__ QOp<KIND> s_q[G::kQLds ? G::kQK * kWave : 1];
 
   const int lane = lane_id(), ln16 = lane & 15, grp = lane >> 4;
@@ -719,7 +723,8 @@ __global__ __launch_bounds__(kWave) void qsa_merge_kernel(AttnParams p) {
 // memory round trips (list positions, block table, first tile, partial
 // store), so launches with few items spread each item over more waves and
 // run in one wave of workgroups where they can: at two waves per SIMD the
-// chip holds 2048 waves.  Large launches (prefill) keep 4 waves per item.
+// chip holds 2048 waves (8 per item up to 256 items, 4 up to 512, 2 up to
+// 1024, 1 up to 2048).  Large launches (prefill) keep 4 waves per item.
 template <int KIND, int D, int NW>
 hipError_t launch_knw(const AttnParams& p, unsigned grid, hipStream_t s) {
   qsa_attn16_kernel<KIND, D, NW><<<grid, dim3(NW * kWave), 0, s>>>(p);
@@ -732,6 +737,7 @@ hipError_t launch_kd(const AttnParams& p, hipStream_t s) {
   const unsigned grid = (unsigned)items;
   if (items <= 256) return launch_knw<KIND, D, 8>(p, grid, s);
   if (items > 512 && items <= 1024) return launch_knw<KIND, D, 2>(p, grid, s);
+  if (items > 1024 && items <= 2048) return launch_knw<KIND, D, 1>(p, grid, s);
   return launch_knw<KIND, D, 4>(p, grid, s);
 }
 

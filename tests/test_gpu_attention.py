@@ -97,13 +97,13 @@ def test_decode_splits(kind, P):
 @pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("D", [128, 256])
 def test_workgroup_shapes(kind, D):
-    """40 rows x 2 KV heads x P partitions = 80 .. 1280 workgroup items: the
-    launch spreads an item over 8, 4 or 2 waves by item count, and every
+    """40 rows x 2 KV heads x P partitions = 80 .. 2560 workgroup items: the
+    launch spreads an item over 8, 4, 2 or 1 waves by item count, and every
     shape must give the oracle's result."""
     w = small_workload(seed=23, D=D, rows=40, topk=150)
     c, oc = _setup(kind, w)
     ro, rl = oracle_attention(oc, w)
-    for P in [1, 4, 8, 16]:
+    for P in [1, 4, 8, 16, 32]:
         say("wg shapes", kind, D, "P", P)
         o, l = run_attention(c, w, num_splits=P, decode=P > 1)
         check(o, l, ro, rl, "wg shapes %s D%d P%d" % (kind, D, P))
