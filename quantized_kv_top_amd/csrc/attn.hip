@@ -11,7 +11,8 @@
 // is applied once after normalization or after the split-K merge).
 //
 // Work decomposition
-//   One workgroup (4 waves) per (row, KV head, split partition).  The
+//   One workgroup per (row, KV head, split partition), of 1, 2, 4 or 8
+//   waves by launch size (see launch_kd).  The
 //   workgroup first resolves the partition's positions to slots (index ->
 //   block table -> slot) into LDS, then its waves take the partition's
 //   tiles of 16 tokens round-robin, keeping kDepth tiles of gathered rows in
@@ -53,6 +54,7 @@ namespace {
 // most 4 per thread (more would cost registers at one wave per workgroup)
 template <int NW>
 constexpr int pos_per_thread() { return 1024 / (NW * 64) < 4 ? 1024 / (NW * 64) : 4; }
+
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kMaxSlack = 8.f;      // log2 units the running max may lag behind
 constexpr float kSigSlack = 16.f;     // factor sigma may lag behind a tile's V scale
