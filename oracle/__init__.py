@@ -22,6 +22,12 @@ five web pages the method is taken from):
   fp64 dequantization, dense fp64 softmax attention over each row's top-k list,
   and the split-K partition rule (page "[Perf][SM70][FP8] Hoist QSA E4M3 KV
   scales", section "Changes").
+* ``calib``     -- per-tensor calibration statistics of an E4M3 cache source
+  (max-abs, nearest-rank percentiles, saturation and low-magnitude counts at
+  a scale; page "[Model][SM70][FP8] Add calibrated E4M3 QSA KV cache").
+* ``topk``      -- top-k selection of each row's positions from indexer
+  scores, and the selection-overlap metrics (same page, validated contract
+  and validation sections).
 * ``brute``     -- pure-Python-loop versions of the same steps for tiny
   inputs; used only to pin the vectorized oracle.
 
@@ -30,4 +36,4 @@ the pages' printed constants, library special cases or brute force; nothing is
 "parity unpinned".
 """
 
-from . import formats, cache, attention, brute  # noqa: F401
+from . import formats, cache, attention, brute, calib, topk  # noqa: F401
