@@ -266,6 +266,39 @@ QSAKV_API qkv_status kv_calib_stats(const void *x, int32_t src_dtype, int64_t n,
                                     size_t workspace_bytes, void *stream);
 
 /*
+ * qsa_topk_select -- each query row's top-k list of positions, selected from
+ * indexer scores: the step ahead of the sparse attention ([E4M3-PR]
+ * validated contract: FP16 raw and compressed indexer caches score the
+ * candidates, and "Non-obvious design decisions": the selection reads the
+ * unquantized indexer cache).  The pages give no scoring formula; the
+ * scores are an input here, and the selection is taken in its plainest
+ * reading:
+ *   row r has n = clamp(row_len[r], 0, row_stride) candidates, positions
+ *   0 .. n-1; its list holds the k positions with the largest scores,
+ *   compared as numbers (-0 == +0; NaN ranks below every number, -inf
+ *   included); equal scores are taken in increasing position order; the
+ *   list is written in increasing position order (as qsa_args.topk_idx
+ *   expects) and padded with -1 when n < k (then it lists every candidate).
+ *
+ *   scores       device [num_rows][row_stride] of score_dtype (QKV_FP32,
+ *                QKV_FP16 or QKV_BF16), 16-B aligned, with row_stride *
+ *                element size a multiple of 16 bytes (else
+ *                QKV_ERR_ALIGNMENT); only the first n scores of a row are
+ *                read.
+ *   row_len      device int32 [num_rows], 4-B aligned.
+ *   topk         k >= 1.
+ *   topk_idx     device int32 [num_rows][topk], 4-B aligned, written.
+ *   row_stride   0 .. 2^30.
+ * The result is exact (integer positions).  One launch, one workgroup per
+ * row: radix selection of the k-th largest score (three passes over the
+ * row for fp32 scores, two for fp16 / bf16), then a pass in position order
+ * that writes the list.
+ */
+QSAKV_API qkv_status qsa_topk_select(const void *scores, int32_t score_dtype, int32_t num_rows,
+                                     int32_t row_stride, const int32_t *row_len, int32_t topk,
+                                     int32_t *topk_idx, void *stream);
+
+/*
  * qkv_cache_bytes -- sizes of the k, v and kv_scale tensors of a cache of
  * this kind and shape (scale_bytes = 0 for kinds without a side tensor).
  * Bytes per token, K + V, scales included: INT8 and INT8_INLINE

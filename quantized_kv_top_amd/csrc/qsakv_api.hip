@@ -284,6 +284,30 @@ qkv_status kv_calib_stats(const void* x, int32_t src_dtype, int64_t n, float sca
   return finish(qsakv::launch_calib(p, static_cast<hipStream_t>(stream)));
 }
 
+qkv_status qsa_topk_select(const void* scores, int32_t score_dtype, int32_t num_rows,
+                           int32_t row_stride, const int32_t* row_len, int32_t topk,
+                           int32_t* topk_idx, void* stream) {
+  if (score_dtype < QKV_BF16 || score_dtype > QKV_FP32) return QKV_ERR_UNSUPPORTED;
+  if (num_rows < 0 || row_stride < 0 || row_stride > (1 << 30) || topk < 1)
+    return QKV_ERR_BAD_SHAPE;
+  int64_t outs;
+  if (!mul_ok(num_rows, topk, &outs) || outs > INT32_MAX) return QKV_ERR_BAD_SHAPE;
+  if (num_rows == 0) return QKV_OK;
+  if (!scores || !row_len || !topk_idx) return QKV_ERR_NULL;
+  const int64_t esize = score_dtype == QKV_FP32 ? 4 : 2;
+  if (!aligned(scores, 16) || (row_stride * esize) % 16 != 0 || !aligned(row_len, 4) ||
+      !aligned(topk_idx, 4))
+    return QKV_ERR_ALIGNMENT;
+  qsakv::TopkParams p;
+  p.scores = scores;
+  p.row_len = row_len;
+  p.out = topk_idx;
+  p.num_rows = num_rows;
+  p.row_stride = row_stride;
+  p.topk = topk;
+  return finish(qsakv::launch_topk(score_dtype, p, static_cast<hipStream_t>(stream)));
+}
+
 qkv_status qkv_cache_bytes(int32_t kind, int32_t num_blocks, int32_t block_size,
                            int32_t num_kv_heads, int32_t head_dim, size_t* k_bytes,
                            size_t* v_bytes, size_t* scale_bytes) {

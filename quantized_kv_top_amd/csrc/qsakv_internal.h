@@ -45,6 +45,18 @@ struct CalibParams {
 size_t calib_workspace_bytes();
 hipError_t launch_calib(const CalibParams& p, hipStream_t s);
 
+// Top-k selection from indexer scores; validated by the caller.
+struct TopkParams {
+  const void* scores;     // [num_rows][row_stride]
+  const int32_t* row_len; // [num_rows]
+  int32_t* out;           // [num_rows][topk]
+  int32_t num_rows;
+  int32_t row_stride;     // elements; a multiple of the scores per 16 bytes
+  int32_t topk;
+};
+
+hipError_t launch_topk(int src_dtype, const TopkParams& p, hipStream_t s);
+
 // Everything an attention kernel needs; validated by the caller.
 struct AttnParams {
   const void* q;

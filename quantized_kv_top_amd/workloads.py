@@ -28,6 +28,9 @@ The shapes and distributions follow the workloads the pages measure
             top-k 2051 distinct uniform causal; fp16 Q/out (top-k 2051 as on
             page "[Perf][SM70][FP8] Hoist QSA E4M3 KV scales", section "Test
             plan").
+* scores    indexer scores for the top-k selection: the prefill rows
+            (2048 x 32768, N(0,1)) and the decode rows (40 x 131072, N(0,1)
+            plus 2.2 over each row's last 4096 positions).
 * e2e       1 seq, Hq 16 / Hkv 2, D 256, BS 64: 122880 existing tokens, a
             chunk of 8192 new tokens whose rows attend with top-k 1024, then
             8 decode steps (one new token each) with top-k 2048 in the decode
@@ -347,6 +350,43 @@ def e2e(pool_blocks, device="cpu", seed=5, ctx0=122880, chunk=8192, steps=8,
 # ---------------------------------------------------------------------------
 # host views for the oracle (numpy; bf16 as uint16 bit patterns)
 # ---------------------------------------------------------------------------
+
+# ---------------------------------------------------------------------------
+# indexer scores (inputs of the top-k selection)
+# ---------------------------------------------------------------------------
+
+@dataclass
+class ScoreSet:
+    name: str
+    scores: torch.Tensor     # [R][stride] fp32 / fp16 / bf16
+    row_len: np.ndarray      # int32 [R]: candidates per row (its position + 1)
+    topk: int
+
+
+def prefill_scores(device="cpu", seed=12, num_rows=2048, ctx=32768, topk=1024,
+                   dtype=torch.float32):
+    """Scores of the prefill rows (positions ctx-2048 .. ctx-1) over their
+    causal prefixes, N(0,1): the top-k of iid scores is a uniform causal
+    subset, as the prefill workload's lists are."""
+    pos = np.arange(ctx - num_rows, ctx)
+    return ScoreSet("prefill", normal((num_rows, ctx), seed, device, dtype),
+                    (pos + 1).astype(np.int32), topk)
+
+
+def decode_scores(device="cpu", seed=13, num_seqs=8, ctx=131072, rows_per_seq=5, topk=2048,
+                  window=4096, boost=2.2, dtype=torch.float32):
+    """Scores of the decode rows (rows_per_seq per sequence at ctx-5 .. ctx-1):
+    N(0,1) plus ``boost`` over each row's last ``window`` positions, so that
+    the top-2048 holds about 1434 recent and 614 earlier positions, the mix
+    of the decode workload's lists."""
+    R = num_seqs * rows_per_seq
+    pos = np.tile(np.arange(ctx - rows_per_seq, ctx), num_seqs)
+    x = normal((R, ctx), seed, device, torch.float32)
+    cols = torch.arange(ctx, device=device)[None, :]
+    p = torch.as_tensor(pos, device=device)[:, None]
+    x += boost * ((cols > p - window) & (cols <= p)).to(torch.float32)
+    return ScoreSet("decode", x.to(dtype), (pos + 1).astype(np.int32), topk)
+
 
 def to_numpy_src(t):
     """A torch tensor -> numpy array the oracle accepts (bf16 -> uint16 bits)."""

@@ -188,3 +188,27 @@ def test_calib_struct_and_validation():
     assert _calib(ws=None) == qsakv.ERR_WORKSPACE
     assert _calib(ws=DUMMY + 128) == qsakv.ERR_WORKSPACE
     assert _calib(wsb=L.qkv_calib_workspace_bytes() - 1) == qsakv.ERR_WORKSPACE
+
+
+def _topk(sc=DUMMY, dt=qsakv.FP32, R=4, stride=1024, rl=DUMMY, k=16, out=DUMMY):
+    return qsakv.lib().qsa_topk_select(sc, dt, R, stride, rl, k, out, None)
+
+
+def test_topk_validation():
+    """Every rejection of qsa_topk_select happens before a launch; no rows is
+    a no-op."""
+    assert _topk(dt=3) == qsakv.ERR_UNSUPPORTED
+    assert _topk(R=-1) == qsakv.ERR_BAD_SHAPE
+    assert _topk(stride=-4) == qsakv.ERR_BAD_SHAPE
+    assert _topk(stride=(1 << 30) + 4) == qsakv.ERR_BAD_SHAPE
+    assert _topk(k=0) == qsakv.ERR_BAD_SHAPE
+    assert _topk(R=1 << 20, k=4096) == qsakv.ERR_BAD_SHAPE      # R * k >= 2^31
+    assert _topk(R=0, sc=None, rl=None, out=None) == qsakv.OK
+    assert _topk(sc=None) == qsakv.ERR_NULL
+    assert _topk(rl=None) == qsakv.ERR_NULL
+    assert _topk(out=None) == qsakv.ERR_NULL
+    assert _topk(sc=DUMMY + 8) == qsakv.ERR_ALIGNMENT
+    assert _topk(stride=1022) == qsakv.ERR_ALIGNMENT            # 4088 B rows
+    assert _topk(dt=qsakv.FP16, stride=1020) == qsakv.ERR_ALIGNMENT
+    assert _topk(rl=DUMMY + 2) == qsakv.ERR_ALIGNMENT
+    assert _topk(out=DUMMY + 2) == qsakv.ERR_ALIGNMENT
