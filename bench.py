@@ -12,7 +12,7 @@ decode (8 x 128K, 40 rows, top-k 2048, split-K 8), e4m3 (12 layers, 4 rows,
 top-k 2051, split-K 8 or 1), mixed (12 E4M3 layers x a 46 + 1 + 1 + 1 row
 batch in one launch), e2e (chunk write + prefill + 8 decode steps), calib
 (E4M3 calibration statistics of 24 K/V tensors), write (quantize-on-write
-throughput).
+throughput), topk (top-k selection of the lists from indexer scores).
 """
 
 import argparse
@@ -445,6 +445,57 @@ def bench_calib(args):
                        "layer0_k": res[0], "layer0_v": res[1]}}
 
 
+def bench_topk(args):
+    """Top-k selection from indexer scores: the prefill rows (2048 x 32768
+    fp32 scores, top-1024; the value), the same in fp16 (two score sets
+    rotated) and the decode rows (40 x 131072 fp32, top-2048; 16 sets
+    rotated).  Algorithmic bytes: the candidates' scores read once plus the
+    lists written."""
+    stream = torch.cuda.current_stream()
+    arms = {}
+    for name, sets in (("prefill_fp32", [wl.prefill_scores("cuda", seed=12)]),
+                       ("prefill_fp16", [wl.prefill_scores("cuda", seed=12 + i, dtype=torch.float16)
+                                         for i in range(2)]),
+                       ("decode_fp32", [wl.decode_scores("cuda", seed=13 + i) for i in range(16)])):
+        s0 = sets[0]
+        R, k = s0.scores.shape[0], s0.topk
+        lens = [torch.from_numpy(s.row_len).cuda() for s in sets]
+        outs = [torch.empty((R, k), dtype=torch.int32, device="cuda") for _ in sets]
+        n = len(sets)
+        total, per, _ = timed_loop(lambda i: qsakv.qsa_topk_select(sets[i % n].scores, lens[i % n], k,
+                                                                   outs[i % n], stream=stream),
+                                   args.steps, args.warmup, stream)
+        ms = total / args.steps
+        b = int(s0.row_len.astype(np.int64).sum()) * s0.scores.element_size() + R * k * 4
+        arms[name] = {"rows": R, "row_stride": s0.scores.shape[1], "topk": k, "ms": ms,
+                      "rows_per_s": R / (ms / 1e3), "GBps": b / (ms / 1e3) / 1e9,
+                      "bytes_per_call": b, "hbm_frac": b / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS}
+        log("topk", name, "%.4f ms" % ms)
+        del sets, lens, outs
+    a = arms["prefill_fp32"]
+    return {"metric": "top-k selection rows/s (indexer scores -> sparse-attention lists)",
+            "value": a["rows_per_s"], "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": a["ms"], "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+            "config": {"workload": "qsa_topk_select: 2048 prefill rows x 32768 fp32 scores "
+                                   "(row r scores its causal prefix), top-1024",
+                       "arms": arms},
+            "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_topk()}
+
+
+def cpu_baseline_topk(rows=2048):
+    """The selection oracle, as it stands (numpy, one process), on the first
+    prefill rows' fp32 scores."""
+    from oracle import topk as otopk
+    s = wl.prefill_scores("cpu", seed=12)
+    src = s.scores[:rows].numpy()
+    t0 = time.perf_counter()
+    otopk.topk_select(src, "fp32", s.row_len[:rows], s.topk)
+    el = time.perf_counter() - t0
+    return {"value": rows / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": "%d prefill rows (32K fp32 scores each, top-1024) in %.1f s" % (rows, el)}
+
+
 class E2ELayer:
     """One layer of the end-to-end step in its own 13.75 GiB pool: the
     existing context written once; the chunk, its prefill and the decode
@@ -610,7 +661,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="prefill",
                     choices=["prefill", "decode", "e4m3", "mixed", "e2e", "calib", "write",
-                             "copy"])
+                             "topk", "copy"])
     ap.add_argument("--layers", type=int, default=0)
     ap.add_argument("--splits", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -627,7 +678,7 @@ def main():
     qsakv.lib()
     fn = {"prefill": bench_prefill, "decode": bench_decode, "e4m3": bench_e4m3,
           "mixed": bench_mixed, "e2e": bench_e2e, "calib": bench_calib, "write": bench_write,
-          "copy": bench_copy}[args.config]
+          "topk": bench_topk, "copy": bench_copy}[args.config]
     print(json.dumps(fn(args)), flush=True)
 
 

@@ -71,6 +71,26 @@ def test_monotone_constant_and_clamped_rows():
         _check(rows, lens, k, "monotone k=%d" % k)
 
 
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+def test_long_16bit_rows(dtype):
+    """16-bit rows of up to 65536 scores (the widest register-held rows)."""
+    x = wl.normal((6, 65536), seed=9, device="cuda", dtype=dtype)
+    lens = np.array([65536, 65535, 40000, 32769, 2049, 65536], np.int32)
+    _check(x, lens, 2048, "long 16-bit rows")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_bin_overflow_falls_back_to_streaming(dtype):
+    """More candidates share the k-th score's top digit than LDS holds
+    (scores drawn from 3 values): the remaining digits re-read the row."""
+    rng = np.random.default_rng(10)
+    v = np.array([0.25, 0.5, 0.75], np.float32)[rng.integers(0, 3, size=(5, 30000))]
+    x = torch.from_numpy(v).to(dtype).cuda()
+    lens = np.array([30000, 29999, 20000, 12000, 9000], np.int32)
+    for k in (1, 1000, 5000):
+        _check(x, lens, k, "bin overflow k=%d" % k)
+
+
 def test_strided_rows():
     """Rows of a wider buffer (row stride above the row length)."""
     base = wl.normal((9, 3000), seed=4, device="cuda", dtype=torch.float16)
