@@ -461,9 +461,12 @@ def bench_topk(args):
         R, k = s0.scores.shape[0], s0.topk
         lens = [torch.from_numpy(s.row_len).cuda() for s in sets]
         outs = [torch.empty((R, k), dtype=torch.int32, device="cuda") for _ in sets]
+        nb = qsakv.qsa_topk_workspace_bytes(R, s0.scores.shape[1], k)
+        ws = torch.empty(nb, dtype=torch.uint8, device="cuda") if nb else None
         n = len(sets)
         total, per, _ = timed_loop(lambda i: qsakv.qsa_topk_select(sets[i % n].scores, lens[i % n], k,
-                                                                   outs[i % n], stream=stream),
+                                                                   outs[i % n], workspace=ws,
+                                                                   stream=stream),
                                    args.steps, args.warmup, stream)
         ms = total / args.steps
         b = int(s0.row_len.astype(np.int64).sum()) * s0.scores.element_size() + R * k * 4

@@ -289,14 +289,24 @@ QSAKV_API qkv_status kv_calib_stats(const void *x, int32_t src_dtype, int64_t n,
  *   topk         k >= 1.
  *   topk_idx     device int32 [num_rows][topk], 4-B aligned, written.
  *   row_stride   0 .. 2^30.
- * The result is exact (integer positions).  One launch, one workgroup per
- * row: radix selection of the k-th largest score (three passes over the
- * row for fp32 scores, two for fp16 / bf16), then a pass in position order
- * that writes the list.
+ *   workspace    device, >= qsa_topk_workspace_bytes(num_rows, row_stride,
+ *                topk) bytes, 256-B aligned; may be NULL when that is 0
+ *                (rows of up to 32768 scores).  Contents on entry are
+ *                ignored; calls sharing a workspace must not overlap in time.
+ * The result is exact (integer positions).  Rows of up to 32768 scores: one
+ * launch, one workgroup per row (the row read once into registers, radix
+ * selection of the k-th largest score, then the list in position order).
+ * Longer rows: segments of 8K-32K scores select their own top k into the
+ * workspace, then one workgroup per row selects from those lists (two
+ * launches); when the lists would not fit one workgroup, one workgroup per
+ * row streams the row for every radix pass instead.
  */
+QSAKV_API size_t qsa_topk_workspace_bytes(int32_t num_rows, int32_t row_stride, int32_t topk);
+
 QSAKV_API qkv_status qsa_topk_select(const void *scores, int32_t score_dtype, int32_t num_rows,
                                      int32_t row_stride, const int32_t *row_len, int32_t topk,
-                                     int32_t *topk_idx, void *stream);
+                                     int32_t *topk_idx, void *workspace, size_t workspace_bytes,
+                                     void *stream);
 
 /*
  * qkv_cache_bytes -- sizes of the k, v and kv_scale tensors of a cache of

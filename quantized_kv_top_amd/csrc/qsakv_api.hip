@@ -181,6 +181,28 @@ size_t ws_bytes(int64_t rows, int64_t heads, int64_t d, int64_t splits) {
   return (size_t)(l.o_bytes + l.ml_bytes);
 }
 
+// Workspace of qsa_topk_select: segment lists' keys, then positions, each
+// [num_rows][row_slots] and 256-B aligned.
+struct TopkWs {
+  int seg_len = 0;
+  int64_t row_slots = 0, key_bytes = 0, bytes = 0;
+};
+
+bool topk_ws(int64_t rows, int64_t stride, int64_t k, TopkWs* w) {
+  *w = TopkWs{};
+  if (rows < 0 || stride < 0 || stride > (1 << 30) || k < 1 || k > INT32_MAX) return false;
+  w->seg_len = qsakv::topk_segment_len(stride, (int32_t)k);
+  if (w->seg_len == 0) return true;
+  const int64_t segs = (stride + w->seg_len - 1) / w->seg_len;
+  w->row_slots = (segs * k + 3) / 4 * 4;
+  int64_t n;
+  if (!mul_ok(rows, w->row_slots, &n) || !mul_ok(n, 4, &w->key_bytes)) return false;
+  w->key_bytes = (w->key_bytes + 255) / 256 * 256;
+  if (w->key_bytes > kI64Max / 2) return false;
+  w->bytes = 2 * w->key_bytes;
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -284,27 +306,43 @@ qkv_status kv_calib_stats(const void* x, int32_t src_dtype, int64_t n, float sca
   return finish(qsakv::launch_calib(p, static_cast<hipStream_t>(stream)));
 }
 
+size_t qsa_topk_workspace_bytes(int32_t num_rows, int32_t row_stride, int32_t topk) {
+  TopkWs w;
+  return topk_ws(num_rows, row_stride, topk, &w) ? (size_t)w.bytes : 0;
+}
+
 qkv_status qsa_topk_select(const void* scores, int32_t score_dtype, int32_t num_rows,
                            int32_t row_stride, const int32_t* row_len, int32_t topk,
-                           int32_t* topk_idx, void* stream) {
+                           int32_t* topk_idx, void* workspace, size_t workspace_bytes,
+                           void* stream) {
   if (score_dtype < QKV_BF16 || score_dtype > QKV_FP32) return QKV_ERR_UNSUPPORTED;
   if (num_rows < 0 || row_stride < 0 || row_stride > (1 << 30) || topk < 1)
     return QKV_ERR_BAD_SHAPE;
   int64_t outs;
   if (!mul_ok(num_rows, topk, &outs) || outs > INT32_MAX) return QKV_ERR_BAD_SHAPE;
+  TopkWs w;
+  if (!topk_ws(num_rows, row_stride, topk, &w)) return QKV_ERR_BAD_SHAPE;
   if (num_rows == 0) return QKV_OK;
   if (!scores || !row_len || !topk_idx) return QKV_ERR_NULL;
   const int64_t esize = score_dtype == QKV_FP32 ? 4 : 2;
   if (!aligned(scores, 16) || (row_stride * esize) % 16 != 0 || !aligned(row_len, 4) ||
       !aligned(topk_idx, 4))
     return QKV_ERR_ALIGNMENT;
-  qsakv::TopkParams p;
+  if (w.bytes > 0 && (!workspace || workspace_bytes < (size_t)w.bytes || !aligned(workspace, 256)))
+    return QKV_ERR_WORKSPACE;
+  qsakv::TopkParams p{};
   p.scores = scores;
   p.row_len = row_len;
   p.out = topk_idx;
   p.num_rows = num_rows;
   p.row_stride = row_stride;
   p.topk = topk;
+  p.seg_len = w.seg_len;
+  p.row_slots = (int32_t)w.row_slots;
+  if (w.bytes > 0) {
+    p.ws_key = static_cast<uint32_t*>(workspace);
+    p.ws_pos = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + w.key_bytes);
+  }
   return finish(qsakv::launch_topk(score_dtype, p, static_cast<hipStream_t>(stream)));
 }
 

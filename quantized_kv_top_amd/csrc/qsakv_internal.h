@@ -53,8 +53,14 @@ struct TopkParams {
   int32_t num_rows;
   int32_t row_stride;     // elements; a multiple of the scores per 16 bytes
   int32_t topk;
+  int32_t seg_len;        // > 0: long rows split into segments of this length
+  int32_t row_slots;      // segments * topk rounded up to 4: workspace entries per row
+  uint32_t* ws_key;       // segments' lists [num_rows][row_slots] (seg_len > 0)
+  int32_t* ws_pos;
 };
 
+// Segment length that qsa_topk_select splits rows of this stride into (0: none).
+int topk_segment_len(int64_t row_stride, int32_t topk);
 hipError_t launch_topk(int src_dtype, const TopkParams& p, hipStream_t s);
 
 // Everything an attention kernel needs; validated by the caller.

@@ -191,32 +191,70 @@ __device__ __forceinline__ uint32_t pick_digit(Smem& s, const uint32_t* h, int s
   return cnt;
 }
 
-// One tile of the list, in position order: V elements per thread (pos < 0:
+// ---- where a row's keys come from and where its list goes ----------------------
+// Scores of one row (or of one segment of it): element idx is the score at
+// position pos0 + idx.
+template <int SRC>
+struct ScoreRow {
+  static constexpr int kVec = Src<SRC>::kVec;
+  const u32x4* data;      // 16-byte groups of the row (segment)
+  int n;                  // elements in play
+  int pos0;
+  __device__ uint32_t key(const u32x4& v, int e) const { return score_key(Src<SRC>::at(v, e)); }
+  __device__ int pos(int idx) const { return pos0 + idx; }
+};
+// The segments' lists of one row, concatenated: keys already mapped, the
+// positions beside them.
+struct KeyRow {
+  static constexpr int kVec = 4;
+  const u32x4* data;
+  int n;
+  const int32_t* posv;
+  __device__ uint32_t key(const u32x4& v, int e) const { return v[e]; }
+  __device__ int pos(int idx) const { return posv[idx]; }
+};
+// The final list: positions.
+struct ListOut {
+  int32_t* out;
+  __device__ void put(uint32_t slot, uint32_t, int pos) const { out[slot] = pos; }
+};
+// A segment's list: keys and positions, for the merge.
+struct PairOut {
+  uint32_t* key;
+  int32_t* pos;
+  __device__ void put(uint32_t slot, uint32_t k, int p) const {
+    key[slot] = k;
+    pos[slot] = p;
+  }
+};
+
+// One tile of the list, in position order: V elements per thread (idx < 0:
 // none); with T the k-th largest key and `ties` the number of keys == T to
 // list, an element goes to slot (#keys > T before it) + min(#keys == T
 // before it, ties) if its key is > T, or if it is one of the first `ties`
 // keys == T.
-template <int V>
-__device__ __forceinline__ void emit_tile(BlockScan& bs, const uint32_t (&key)[V],
-                                          const int (&pos)[V], uint32_t T, uint32_t ties,
-                                          uint32_t& gt_base, uint32_t& eq_base, int32_t* out) {
+template <int V, typename R, typename O>
+__device__ __forceinline__ void emit_tile(BlockScan& bs, const R& row, const O& o,
+                                          const uint32_t (&key)[V], const int (&idx)[V],
+                                          uint32_t T, uint32_t ties, uint32_t& gt_base,
+                                          uint32_t& eq_base) {
   uint32_t cg = 0, ce = 0;
 #pragma unroll
   for (int e = 0; e < V; ++e) {
-    cg += (pos[e] >= 0 && key[e] > T) ? 1u : 0u;
-    ce += (pos[e] >= 0 && key[e] == T) ? 1u : 0u;
+    cg += (idx[e] >= 0 && key[e] > T) ? 1u : 0u;
+    ce += (idx[e] >= 0 && key[e] == T) ? 1u : 0u;
   }
   uint32_t tot;
   const uint32_t before = bs.exscan(cg | (ce << 16), &tot);   // < 2^16 per tile
   uint32_t gb = gt_base + (before & 0xffffu), eb = eq_base + (before >> 16);
 #pragma unroll
   for (int e = 0; e < V; ++e) {
-    if (pos[e] < 0) continue;
+    if (idx[e] < 0) continue;
     if (key[e] > T) {
-      out[gb + min(eb, ties)] = pos[e];
+      o.put(gb + min(eb, ties), key[e], row.pos(idx[e]));
       ++gb;
     } else if (key[e] == T) {
-      if (eb < ties) out[gb + eb] = pos[e];
+      if (eb < ties) o.put(gb + eb, key[e], row.pos(idx[e]));
       ++eb;
     }
   }
@@ -226,53 +264,55 @@ __device__ __forceinline__ void emit_tile(BlockScan& bs, const uint32_t (&key)[V
 
 // ---- passes that stream the row from memory ---------------------------------
 // (the histograms are clear and published by a barrier before the first)
-template <int SRC>
-__device__ void stream_passes(Smem& s, const u32x4* row, int n, int first, Sel& st) {
-  constexpr int kVec = Src<SRC>::kVec;
-  const int nvec = (n + kVec - 1) / kVec;
+template <typename R>
+__device__ void stream_passes(Smem& s, const R& row, int first, Sel& st) {
+  constexpr int kVec = R::kVec;
+  const int nvec = (row.n + kVec - 1) / kVec;
 #pragma unroll
   for (int pass = 0; pass < kPasses; ++pass) {
     if (pass < first) continue;
     const uint32_t dmask = (1u << kWidth[pass]) - 1u;
     for (int g = threadIdx.x; g < nvec; g += kThreads) {
-      const u32x4 v = row[g];
+      const u32x4 v = row.data[g];
 #pragma unroll
       for (int e = 0; e < kVec; ++e)
-        if (g * kVec + e < n)
-          count_key(s.hist[pass], score_key(Src<SRC>::at(v, e)), st, kShift[pass], dmask);
+        if (g * kVec + e < row.n) count_key(s.hist[pass], row.key(v, e), st, kShift[pass], dmask);
     }
     __syncthreads();
     pick_digit(s, s.hist[pass], kShift[pass], kWidth[pass], st);
   }
 }
 
-template <int SRC>
-__device__ void stream_emit(BlockScan& bs, const u32x4* row, int n, const Sel& st, int k,
-                            int32_t* out) {
-  constexpr int kVec = Src<SRC>::kVec;
-  const int nvec = (n + kVec - 1) / kVec;
+template <typename R, typename O>
+__device__ void stream_emit(BlockScan& bs, const R& row, const O& o, const Sel& st, int k) {
+  constexpr int kVec = R::kVec;
+  const int nvec = (row.n + kVec - 1) / kVec;
   const uint32_t T = st.pval, ties = st.need, n_gt = (uint32_t)k - ties;
   uint32_t gt_base = 0, eq_base = 0;
   for (int g0 = 0; g0 < nvec; g0 += kThreads) {
     const int g = g0 + (int)threadIdx.x;
-    const u32x4 v = g < nvec ? row[g] : u32x4{0u, 0u, 0u, 0u};
+    const u32x4 v = g < nvec ? row.data[g] : u32x4{0u, 0u, 0u, 0u};
     uint32_t key[kVec];
-    int pos[kVec];
+    int idx[kVec];
 #pragma unroll
     for (int e = 0; e < kVec; ++e) {
-      key[e] = score_key(Src<SRC>::at(v, e));
-      pos[e] = (g < nvec && g * kVec + e < n) ? g * kVec + e : -1;
+      key[e] = row.key(v, e);
+      idx[e] = (g < nvec && g * kVec + e < row.n) ? g * kVec + e : -1;
     }
-    emit_tile<kVec>(bs, key, pos, T, ties, gt_base, eq_base, out);
+    emit_tile<kVec>(bs, row, o, key, idx, T, ties, gt_base, eq_base);
     if (gt_base == n_gt && eq_base >= ties) break;   // uniform: the list is complete
   }
 }
 
-// rows with at most k candidates list all of them
-__device__ __forceinline__ bool list_all(int n, int k, int32_t* out) {
-  if (n > k) return false;
-  for (int i = threadIdx.x; i < k; i += kThreads) out[i] = i < n ? i : -1;
-  return true;
+// The whole row streamed (rows beyond the register capacity).
+template <typename R, typename O>
+__device__ void stream_select(Smem& s, const R& row, const O& o, int k) {
+  BlockScan bs{s};
+  Sel st{0u, 0u, (uint32_t)k};
+  clear_hists(s);
+  __syncthreads();
+  stream_passes(s, row, 0, st);
+  stream_emit(bs, row, o, st, k);
 }
 
 template <int SRC>
@@ -281,37 +321,39 @@ __device__ __forceinline__ const u32x4* row_ptr(const TopkParams& p, int r) {
                                         (int64_t)r * p.row_stride * (SRC == kDtFP32 ? 4 : 2));
 }
 
-// Rows beyond the register capacity: every pass streams the row.
-template <int SRC>
-__global__ __launch_bounds__(kThreads) void topk_stream_kernel(TopkParams p) {
-  __shared__ Smem s;
-  const int r = blockIdx.x, k = p.topk;
-  int32_t* out = p.out + (int64_t)r * k;
-  const int n = min(max(p.row_len[r], 0), p.row_stride);
-  if (list_all(n, k, out)) return;
-  const u32x4* row = row_ptr<SRC>(p, r);
-  BlockScan bs{s};
-  Sel st{0u, 0u, (uint32_t)k};
-  clear_hists(s);
-  __syncthreads();
-  stream_passes<SRC>(s, row, n, 0, st);
-  stream_emit<SRC>(bs, row, n, st, k, out);
-}
+// Registers of a thread for rows of up to KPT * 1024 elements: group j holds
+// the kVec elements at (t + 1024 j) kVec ..; elements at and beyond row.n
+// carry key 0, the lowest, which never reaches the list of a row with more
+// than k elements.
+template <typename R, int KPT>
+struct RegKeys {
+  static constexpr int kVec = R::kVec;
+  static constexpr int kGroups = KPT / kVec;
+  uint32_t key[kGroups][kVec];
+  __device__ void load(const R& row) {
+    const int last = max((row.n + kVec - 1) / kVec, 1) - 1;   // loads clamped to the last group
+    u32x4 raw[kGroups];
+#pragma unroll
+    for (int j = 0; j < kGroups; ++j) raw[j] = row.data[min((int)threadIdx.x + j * kThreads, last)];
+#pragma unroll
+    for (int j = 0; j < kGroups; ++j)
+#pragma unroll
+      for (int e = 0; e < kVec; ++e)
+        key[j][e] = ((int)threadIdx.x + j * kThreads) * kVec + e < row.n ? row.key(raw[j], e) : 0u;
+  }
+};
 
-// One row whose keys a thread holds in registers (group j of thread t: the
-// kVec scores at positions (t + 1024 j) kVec ..; positions beyond the row's
-// n carry key 0, the lowest, which never reaches the list of a row with more
-// than k candidates): the first digit from registers, then the keys of its
-// bin and above (the candidates) to LDS in position order and the remaining
-// digits over them -- or, when the candidates overflow LDS (heavy ties), the
-// remaining passes re-read the row.
-template <int SRC, int KPT>
-__device__ __forceinline__ void select_row(Smem& s, uint32_t* s_key, int32_t* s_pos,
-                                           const uint32_t (&key)[KPT / Src<SRC>::kVec]
-                                                                [Src<SRC>::kVec],
-                                           const u32x4* row, int n, int k, int32_t* out) {
-  constexpr int kVec = Src<SRC>::kVec;
+// One row held in registers, more than k elements: the first digit from
+// registers, then the keys of its bin and above (the candidates) to LDS in
+// position order and the remaining digits over them -- or, when the
+// candidates overflow LDS (heavy ties), the remaining passes re-read the row.
+template <typename R, int KPT, typename O>
+__device__ __forceinline__ void select_row(Smem& s, uint32_t* s_key, int32_t* s_idx,
+                                           const RegKeys<R, KPT>& rk, const R& row, const O& o,
+                                           int k) {
+  constexpr int kVec = R::kVec;
   constexpr int kGroups = KPT / kVec;
+  const auto& key = rk.key;
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int w = (int)uniform(tid / kWave);
@@ -331,8 +373,8 @@ __device__ __forceinline__ void select_row(Smem& s, uint32_t* s_key, int32_t* s_
   const uint32_t lo = st.pval;                           // d0 << kShift[0]
   const uint32_t ncand = (uint32_t)k - st.need + bin0;
   if (ncand > (uint32_t)kCand) {                         // uniform
-    stream_passes<SRC>(s, row, n, 1, st);
-    stream_emit<SRC>(bs, row, n, st, k, out);
+    stream_passes(s, row, 1, st);
+    stream_emit(bs, row, o, st, k);
     return;
   }
 
@@ -375,14 +417,14 @@ __device__ __forceinline__ void select_row(Smem& s, uint32_t* s_key, int32_t* s_
       const uint32_t start = sg < kWave
           ? __builtin_amdgcn_readlane(i0, sg) - __builtin_amdgcn_readlane(c0, sg)
           : __builtin_amdgcn_readlane(i1, sg - kWave) - __builtin_amdgcn_readlane(c1, sg - kWave);
-      uint32_t o = start + ((wincl[j / 3] >> (10 * (j % 3))) & 0x3ffu) - cnt[j];
+      uint32_t oo = start + ((wincl[j / 3] >> (10 * (j % 3))) & 0x3ffu) - cnt[j];
       const int base = (tid + j * kThreads) * kVec;
 #pragma unroll
       for (int e = 0; e < kVec; ++e) {
         if (key[j][e] >= lo) {
-          s_key[o] = key[j][e];
-          s_pos[o] = base + e;
-          ++o;
+          s_key[oo] = key[j][e];
+          s_idx[oo] = base + e;
+          ++oo;
         }
       }
     }
@@ -405,47 +447,153 @@ __device__ __forceinline__ void select_row(Smem& s, uint32_t* s_key, int32_t* s_
   for (int c0 = 0; c0 < (int)ncand; c0 += kThreads) {
     const int i = c0 + tid;
     const uint32_t kk[1] = {i < (int)ncand ? s_key[i] : 0u};
-    const int pos[1] = {i < (int)ncand ? s_pos[i] : -1};
-    emit_tile<1>(bs, kk, pos, T, ties, gt_base, eq_base, out);
+    const int ix[1] = {i < (int)ncand ? s_idx[i] : -1};
+    emit_tile<1>(bs, row, o, kk, ix, T, ties, gt_base, eq_base);
     if (gt_base == n_gt && eq_base >= ties) break;       // uniform
   }
 }
 
+// ---- kernels --------------------------------------------------------------------
+
+// Rows beyond the register capacity, one workgroup each: every pass streams
+// the row.
+template <int SRC>
+__global__ __launch_bounds__(kThreads) void topk_stream_kernel(TopkParams p) {
+  __shared__ Smem s;
+  const int r = blockIdx.x, k = p.topk;
+  int32_t* out = p.out + (int64_t)r * k;
+  const int n = min(max(p.row_len[r], 0), p.row_stride);
+  if (n <= k) {
+    for (int i = threadIdx.x; i < k; i += kThreads) out[i] = i < n ? i : -1;
+    return;
+  }
+  stream_select(s, ScoreRow<SRC>{row_ptr<SRC>(p, r), n, 0}, ListOut{out}, k);
+}
+
 // Rows of up to KPT * 1024 scores, one workgroup each, two per CU (8 waves
-// per SIMD, <= 64 registers): the row's 16-byte groups are loaded at once
-// (addresses clamped to the row's last group) and turned into keys.
+// per SIMD, <= 64 registers).
 template <int SRC, int KPT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
 void topk_cand_kernel(TopkParams p) {
-  constexpr int kVec = Src<SRC>::kVec;
-  constexpr int kGroups = KPT / kVec;                   // 16-byte groups per thread
   __shared__ Smem s;
   __shared__ uint32_t s_key[kCand];
-  __shared__ int32_t s_pos[kCand];
-  const int tid = threadIdx.x, k = p.topk, r = blockIdx.x;
+  __shared__ int32_t s_idx[kCand];
+  const int r = blockIdx.x, k = p.topk;
   int32_t* out = p.out + (int64_t)r * k;
   const int n = min(max(p.row_len[r], 0), p.row_stride);
-  if (list_all(n, k, out)) return;
-  const u32x4* row = row_ptr<SRC>(p, r);
-  const int last = (n + kVec - 1) / kVec - 1;
-  uint32_t key[kGroups][kVec];
-  {
-    u32x4 raw[kGroups];
-#pragma unroll
-    for (int j = 0; j < kGroups; ++j) raw[j] = row[min(tid + j * kThreads, last)];
-#pragma unroll
-    for (int j = 0; j < kGroups; ++j)
-#pragma unroll
-      for (int e = 0; e < kVec; ++e)
-        key[j][e] = (tid + j * kThreads) * kVec + e < n ? score_key(Src<SRC>::at(raw[j], e)) : 0u;
+  if (n <= k) {
+    for (int i = threadIdx.x; i < k; i += kThreads) out[i] = i < n ? i : -1;
+    return;
   }
-  select_row<SRC, KPT>(s, s_key, s_pos, key, row, n, k, out);
+  const ScoreRow<SRC> row{row_ptr<SRC>(p, r), n, 0};
+  RegKeys<ScoreRow<SRC>, KPT> rk;
+  rk.load(row);
+  select_row(s, s_key, s_idx, rk, row, ListOut{out}, k);
 }
+
+// Long rows, stage 1: segment s (positions [s L, (s + 1) L)) of row r
+// selects its own top k into the workspace -- keys and positions, in
+// position order; a segment with at most k elements in play lists them all.
+// The row's top k is among its segments' lists: an element that fewer than
+// k elements of the row rank ahead of has fewer than k ahead of it in its
+// segment too.
+template <int SRC, int KPT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void topk_seg_kernel(TopkParams p) {
+  __shared__ Smem s;
+  __shared__ uint32_t s_key[kCand];
+  __shared__ int32_t s_idx[kCand];
+  const int seg = blockIdx.x, r = blockIdx.y, k = p.topk, L = p.seg_len;
+  const int n = min(max(p.row_len[r], 0), p.row_stride);
+  const int ns = min(max(n - seg * L, 0), L);
+  if (ns == 0) return;
+  const int64_t slot0 = (int64_t)r * p.row_slots + (int64_t)seg * k;
+  const PairOut o{p.ws_key + slot0, p.ws_pos + slot0};
+  const ScoreRow<SRC> row{row_ptr<SRC>(p, r) + (int64_t)seg * L / Src<SRC>::kVec, ns, seg * L};
+  RegKeys<ScoreRow<SRC>, KPT> rk;
+  rk.load(row);
+  if (ns <= k) {                                         // the whole segment, in order
+    constexpr int kVec = Src<SRC>::kVec;
+#pragma unroll
+    for (int j = 0; j < KPT / kVec; ++j)
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) {
+        const int idx = ((int)threadIdx.x + j * kThreads) * kVec + e;
+        if (idx < ns) o.put(idx, rk.key[j][e], row.pos(idx));
+      }
+    return;
+  }
+  select_row(s, s_key, s_idx, rk, row, o, k);
+}
+
+// Long rows, stage 2: the segments' lists of row r, concatenated (every
+// segment before the row's last non-empty one lists exactly k, so the
+// concatenation is dense and in position order), hold the row's top k.
+template <int KPT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void topk_merge_kernel(TopkParams p) {
+  __shared__ Smem s;
+  __shared__ uint32_t s_key[kCand];
+  __shared__ int32_t s_idx[kCand];
+  const int r = blockIdx.x, k = p.topk, L = p.seg_len;
+  int32_t* out = p.out + (int64_t)r * k;
+  const int n = min(max(p.row_len[r], 0), p.row_stride);
+  const int full = n / L, tail = n - full * L;           // full segments, rest of the last
+  const int m = full * k + min(tail, k);                 // listed elements (full * L >= full * k)
+  const int64_t slot0 = (int64_t)r * p.row_slots;      // 16-byte aligned
+  const KeyRow row{reinterpret_cast<const u32x4*>(p.ws_key + slot0), m, p.ws_pos + slot0};
+  if (m <= k) {
+    for (int i = threadIdx.x; i < k; i += kThreads) out[i] = i < m ? row.pos(i) : -1;
+    return;
+  }
+  RegKeys<KeyRow, KPT> rk;
+  rk.load(row);
+  select_row(s, s_key, s_idx, rk, row, ListOut{out}, k);
+}
+
+}  // namespace
+
+// Segment length for split selection of long rows (0: no split): the
+// smallest of 8192, 16384, 32768 that is at least 4 k and keeps the merged
+// lists (segments x k) within the 32768 keys one workgroup holds.
+int topk_segment_len(int64_t row_stride, int32_t topk) {
+  if (row_stride <= (int64_t)kMaxKPT * kThreads) return 0;
+  for (int L = 8192; L <= kMaxKPT * kThreads; L *= 2) {
+    const int64_t segs = (row_stride + L - 1) / L;
+    if (L >= 4 * (int64_t)topk && segs * topk <= (int64_t)kMaxKPT * kThreads) return L;
+  }
+  return 0;
+}
+
+namespace {
 
 template <int SRC>
 hipError_t launch_src(const TopkParams& p, hipStream_t s) {
-  const dim3 grid((unsigned)p.num_rows), block(kThreads);
+  const dim3 block(kThreads);
   const int64_t per_thread = ((int64_t)p.row_stride + kThreads - 1) / kThreads;
+  if (p.seg_len > 0) {
+    const int nseg = (int)((p.row_stride + p.seg_len - 1) / p.seg_len);
+    const int kpt = p.seg_len / kThreads;
+    const dim3 g1((unsigned)nseg, (unsigned)p.num_rows);
+    if (kpt <= 8)
+      topk_seg_kernel<SRC, 8><<<g1, block, 0, s>>>(p);
+    else if (kpt <= 16)
+      topk_seg_kernel<SRC, 16><<<g1, block, 0, s>>>(p);
+    else
+      topk_seg_kernel<SRC, kMaxKPT><<<g1, block, 0, s>>>(p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t merged = (int64_t)nseg * p.topk;
+    const dim3 g2((unsigned)p.num_rows);
+    if (merged <= 8 * kThreads)
+      topk_merge_kernel<8><<<g2, block, 0, s>>>(p);
+    else if (merged <= 16 * kThreads)
+      topk_merge_kernel<16><<<g2, block, 0, s>>>(p);
+    else
+      topk_merge_kernel<kMaxKPT><<<g2, block, 0, s>>>(p);
+    return hipGetLastError();
+  }
+  const dim3 grid((unsigned)p.num_rows);
   if (per_thread <= 8)
     topk_cand_kernel<SRC, 8><<<grid, block, 0, s>>>(p);
   else if (per_thread <= 16)

@@ -25,7 +25,8 @@ KIND_BY_NAME = {"int8": CACHE_INT8, "int8_inline": CACHE_INT8_INLINE,
 
 EXPORTED = ("kv_quant_write", "qsa_sparse_attn_prefill", "qsa_decode_workspace_bytes",
             "qsa_sparse_attn_decode", "qkv_calib_workspace_bytes", "kv_calib_stats",
-            "qsa_topk_select", "qkv_cache_bytes", "qkv_status_str", "qkv_last_hip_error", "qkv_abi_version")
+            "qsa_topk_workspace_bytes", "qsa_topk_select", "qkv_cache_bytes",
+            "qkv_status_str", "qkv_last_hip_error", "qkv_abi_version")
 
 
 class QkvCache(ctypes.Structure):
@@ -81,7 +82,9 @@ def lib():
     L.qkv_calib_workspace_bytes.restype = c_sz
     L.kv_calib_stats.argtypes = [c_vp, c_i32, c_i64, ctypes.c_float, c_vp, c_vp, c_sz, c_vp]
     L.kv_calib_stats.restype = c_i32
-    L.qsa_topk_select.argtypes = [c_vp, c_i32, c_i32, c_i32, c_vp, c_i32, c_vp, c_vp]
+    L.qsa_topk_workspace_bytes.argtypes = [c_i32, c_i32, c_i32]
+    L.qsa_topk_workspace_bytes.restype = c_sz
+    L.qsa_topk_select.argtypes = [c_vp, c_i32, c_i32, c_i32, c_vp, c_i32, c_vp, c_vp, c_sz, c_vp]
     L.qsa_topk_select.restype = c_i32
     L.qkv_cache_bytes.argtypes = [c_i32, c_i32, c_i32, c_i32, c_i32, P(c_sz), P(c_sz), P(c_sz)]
     L.qkv_cache_bytes.restype = c_i32
@@ -228,16 +231,24 @@ def kv_calib_stats(x, scale, out, workspace, stream=None):
            "kv_calib_stats")
 
 
-def qsa_topk_select(scores, row_len, topk, out, stream=None):
+def qsa_topk_workspace_bytes(num_rows, row_stride, topk):
+    return int(lib().qsa_topk_workspace_bytes(num_rows, row_stride, topk))
+
+
+def qsa_topk_select(scores, row_len, topk, out, workspace=None, stream=None):
     """Top-k positions of each row of the device tensor ``scores``
     ([R][row_stride], fp32 / fp16 / bf16, rows contiguous) among the first
     ``row_len[r]`` (device int32 [R]); the library writes the increasing,
-    -1 padded lists into ``out`` (device int32 [R][topk])."""
+    -1 padded lists into ``out`` (device int32 [R][topk]).  ``workspace``: a
+    device uint8 tensor of qsa_topk_workspace_bytes(...) bytes when that is
+    not 0."""
     assert scores.dim() == 2 and scores.stride(1) == 1 and out.is_contiguous()
     R = scores.shape[0]
     assert out.shape == (R, topk) and row_len.numel() == R and row_len.is_contiguous()
+    wb = 0 if workspace is None else workspace.numel()
     _check(lib().qsa_topk_select(_ptr(scores), dtype_code(scores), R, scores.stride(0),
-                                 _ptr(row_len), topk, _ptr(out), _stream(stream)),
+                                 _ptr(row_len), topk, _ptr(out), _ptr(workspace), wb,
+                                 _stream(stream)),
            "qsa_topk_select")
 
 

@@ -60,9 +60,11 @@ int main(void) {
                                            qkv_calib_workspace_bytes(), NULL),
          QKV_ERR_BAD_SCALE);
   expect("topk no k", qsa_topk_select(dummy, QKV_FP32, 4, 1024, (const int32_t *)dummy, 0,
-                                      (int32_t *)dummy, NULL),
+                                      (int32_t *)dummy, NULL, 0, NULL),
          QKV_ERR_BAD_SHAPE);
-  expect("topk no rows", qsa_topk_select(NULL, QKV_FP16, 0, 0, NULL, 1, NULL, NULL), QKV_OK);
+  expect("topk no rows", qsa_topk_select(NULL, QKV_FP16, 0, 0, NULL, 1, NULL, NULL, 0, NULL),
+         QKV_OK);
+  if (qsa_topk_workspace_bytes(40, 131072, 2048) == 0) ++fails;
   if (qsa_decode_workspace_bytes(40, 16, 256, 8) == 0) ++fails;
   if (fails == 0) printf("ok\n");
   return fails == 0 ? 0 : 1;

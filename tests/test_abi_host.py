@@ -190,8 +190,8 @@ def test_calib_struct_and_validation():
     assert _calib(wsb=L.qkv_calib_workspace_bytes() - 1) == qsakv.ERR_WORKSPACE
 
 
-def _topk(sc=DUMMY, dt=qsakv.FP32, R=4, stride=1024, rl=DUMMY, k=16, out=DUMMY):
-    return qsakv.lib().qsa_topk_select(sc, dt, R, stride, rl, k, out, None)
+def _topk(sc=DUMMY, dt=qsakv.FP32, R=4, stride=1024, rl=DUMMY, k=16, out=DUMMY, ws=None, wsb=0):
+    return qsakv.lib().qsa_topk_select(sc, dt, R, stride, rl, k, out, ws, wsb, None)
 
 
 def test_topk_validation():
@@ -212,3 +212,23 @@ def test_topk_validation():
     assert _topk(dt=qsakv.FP16, stride=1020) == qsakv.ERR_ALIGNMENT
     assert _topk(rl=DUMMY + 2) == qsakv.ERR_ALIGNMENT
     assert _topk(out=DUMMY + 2) == qsakv.ERR_ALIGNMENT
+    # long rows need the segment workspace
+    need = qsakv.lib().qsa_topk_workspace_bytes(40, 131072, 2048)
+    assert _topk(R=40, stride=131072, k=2048) == qsakv.ERR_WORKSPACE
+    assert _topk(R=40, stride=131072, k=2048, ws=DUMMY, wsb=need - 1) == qsakv.ERR_WORKSPACE
+    assert _topk(R=40, stride=131072, k=2048, ws=DUMMY + 128, wsb=need) == qsakv.ERR_WORKSPACE
+
+
+def test_topk_workspace_bytes():
+    """Rows of up to 32768 scores need none; longer rows are cut into the
+    smallest of 8K / 16K / 32K-score segments that is at least 4 k and keeps
+    segments x k within 32768: keys and positions, [rows][segments * k
+    rounded up to 4] each, 256-B aligned."""
+    L = qsakv.lib()
+    assert L.qsa_topk_workspace_bytes(2048, 32768, 1024) == 0
+    # 131072 / 8192 = 16 segments x 2048
+    assert L.qsa_topk_workspace_bytes(40, 131072, 2048) == 2 * 40 * 16 * 2048 * 4
+    # 65536 / 16384 = 4 segments (8192 < 4 * 2051) x 2051 -> 8204 slots
+    assert L.qsa_topk_workspace_bytes(4, 65536, 2051) == 2 * ((4 * 8204 * 4 + 255) // 256 * 256)
+    # k too large for segments: streamed, no workspace
+    assert L.qsa_topk_workspace_bytes(4, 1 << 20, 8192) == 0

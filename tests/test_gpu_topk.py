@@ -19,8 +19,11 @@ DTYPES = [torch.float32, torch.float16, torch.bfloat16]
 
 
 def _gpu(scores, row_len, k):
-    out = torch.full((scores.shape[0], k), -7, dtype=torch.int32, device="cuda")
-    qsakv.qsa_topk_select(scores, dev(row_len, torch.int32), k, out)
+    R, stride = scores.shape[0], scores.stride(0)
+    out = torch.full((R, k), -7, dtype=torch.int32, device="cuda")
+    nb = qsakv.qsa_topk_workspace_bytes(R, stride, k)
+    ws = torch.full((nb,), 0xA5, dtype=torch.uint8, device="cuda") if nb else None
+    qsakv.qsa_topk_select(scores, dev(row_len, torch.int32), k, out, workspace=ws)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
@@ -89,6 +92,35 @@ def test_bin_overflow_falls_back_to_streaming(dtype):
     lens = np.array([30000, 29999, 20000, 12000, 9000], np.int32)
     for k in (1, 1000, 5000):
         _check(x, lens, k, "bin overflow k=%d" % k)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("stride,k", [(65536, 2051), (131072, 2048), (40960, 1024)])
+def test_split_rows_ragged(dtype, stride, k):
+    """Rows longer than one workgroup holds: segments select their own top k,
+    then a merge; lengths that end inside, at and before segment edges, and
+    rows with at most k candidates."""
+    lens = [stride, stride - 1, 8192, 8193, 16384 + 5, 3 * k + 1, k, k + 1, 100, 0,
+            stride // 2 + 7, 24575]
+    x = wl.normal((len(lens), stride), seed=stride + k, device="cuda", dtype=dtype)
+    _check(x, np.array(lens, np.int32), k, "split ragged")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_split_rows_ties_and_specials(dtype):
+    """Long rows of a few values with NaN / +-inf / +-0: the cut falls inside
+    runs of equal scores that cross segment edges (and overflow the
+    candidate capacity in places)."""
+    rng = np.random.default_rng(21)
+    pool = np.array([np.nan, np.inf, -np.inf, 0.0, -0.0, 1.0, -1.0, 2.0], np.float32)
+    stride = 65536
+    v = pool[rng.integers(0, pool.size, size=(6, stride))]
+    v[3] = np.nan                     # all NaN
+    v[4, :] = 1.0                     # all equal
+    x = torch.from_numpy(v).to(dtype).cuda()
+    lens = np.array([stride, 60000, 33000, stride, 50001, 40000], np.int32)
+    for k in (1, 2048, 4096):
+        _check(x, lens, k, "split ties k=%d" % k)
 
 
 def test_strided_rows():
