@@ -221,14 +221,19 @@ def test_topk_validation():
 
 def test_topk_workspace_bytes():
     """Rows of up to 32768 scores need none; longer rows are cut into the
-    smallest of 8K / 16K / 32K-score segments that is at least 4 k and keeps
+    largest of 32K / 16K / 8K-score segments that is at least 4 k and keeps
     segments x k within 32768: keys and positions, [rows][segments * k
     rounded up to 4] each, 256-B aligned."""
     L = qsakv.lib()
     assert L.qsa_topk_workspace_bytes(2048, 32768, 1024) == 0
-    # 131072 / 8192 = 16 segments x 2048
-    assert L.qsa_topk_workspace_bytes(40, 131072, 2048) == 2 * 40 * 16 * 2048 * 4
-    # 65536 / 16384 = 4 segments (8192 < 4 * 2051) x 2051 -> 8204 slots
-    assert L.qsa_topk_workspace_bytes(4, 65536, 2051) == 2 * ((4 * 8204 * 4 + 255) // 256 * 256)
+    # 131072 / 32768 = 4 segments x 2048
+    assert L.qsa_topk_workspace_bytes(40, 131072, 2048) == 2 * 40 * 4 * 2048 * 4
+    # 65536 / 32768 = 2 segments x 2051 -> 4102 slots, rounded up to 4104
+    assert L.qsa_topk_workspace_bytes(4, 65536, 2051) == 2 * ((4 * 4104 * 4 + 255) // 256 * 256)
+    # 1M-score rows, k 512: 32K segments (32 x 512 = 16384)
+    assert L.qsa_topk_workspace_bytes(2, 1 << 20, 512) == 2 * 2 * 32 * 512 * 4
+    # 1M-score rows, k 2048: 32 x 2048 > 32768, and shorter segments only
+    # make more lists: streamed, no workspace
+    assert L.qsa_topk_workspace_bytes(4, 1 << 20, 2048) == 0
     # k too large for segments: streamed, no workspace
     assert L.qsa_topk_workspace_bytes(4, 1 << 20, 8192) == 0

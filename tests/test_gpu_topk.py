@@ -100,8 +100,8 @@ def test_split_rows_ragged(dtype, stride, k):
     """Rows longer than one workgroup holds: segments select their own top k,
     then a merge; lengths that end inside, at and before segment edges, and
     rows with at most k candidates."""
-    lens = [stride, stride - 1, 8192, 8193, 16384 + 5, 3 * k + 1, k, k + 1, 100, 0,
-            stride // 2 + 7, 24575]
+    lens = [stride, stride - 1, 32768, 32769, 32767, 3 * k + 1, k, k + 1, 100, 0,
+            stride // 2 + 7, 24575, min(stride, 65536 + 5)]
     x = wl.normal((len(lens), stride), seed=stride + k, device="cuda", dtype=dtype)
     _check(x, np.array(lens, np.int32), k, "split ragged")
 
