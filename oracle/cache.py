@@ -17,6 +17,12 @@ Layouts (per layer; a "slot" is block * block_size + offset):
   per layer for K and one for V (page "[Model][SM70][FP8] Add calibrated E4M3
   QSA KV cache", section "Purpose").
 * ``bf16``        K and V: bf16 ``[slots][Hkv][D]`` (comparison arm).
+* ``nvfp4``       K and V: E2M1 codes packed two per byte ``[slots][Hkv][D/2]``
+  (element 2j in the low nibble of byte j); E4M3 block scales in a side
+  tensor of bytes ``[slots][Hkv][2][D/16]`` (K's blocks, then V's); one
+  float32 scale per layer for K and one for V.  A reading (see
+  ``formats.nvfp4_quantize``): the pages name NVFP4 KV storage only as a
+  variant outside the E4M3 contract.
 
 Each row is held here as raw bytes so that it can be compared bit for bit.
 """
@@ -25,7 +31,7 @@ import numpy as np
 
 from . import formats
 
-KINDS = ("int8", "int8_inline", "e4m3", "bf16")
+KINDS = ("int8", "int8_inline", "e4m3", "bf16", "nvfp4")
 
 
 def row_bytes(kind, head_dim):
@@ -38,6 +44,8 @@ def row_bytes(kind, head_dim):
         return head_dim
     if kind == "bf16":
         return 2 * head_dim
+    if kind == "nvfp4":
+        return head_dim // 2
     raise ValueError(kind)
 
 
@@ -51,6 +59,8 @@ def bytes_per_token(kind, num_kv_heads, head_dim):
     per_row = row_bytes(kind, head_dim)
     if kind == "int8":
         per_row += 4                      # the row's fp32 scale in the side tensor
+    if kind == "nvfp4":
+        per_row += head_dim // formats.NVFP4_BLOCK   # the row's block scales
     return 2 * num_kv_heads * per_row
 
 
@@ -78,10 +88,13 @@ class OracleCache:
         self.v = np.zeros((n, num_kv_heads, rb), dtype=np.uint8)
         self.kv_scale = (np.zeros((n, num_kv_heads, 2), dtype=np.float32)
                          if kind == "int8" else None)
+        if kind == "nvfp4":
+            self.kv_scale = np.zeros((n, num_kv_heads, 2, head_dim // formats.NVFP4_BLOCK),
+                                     dtype=np.uint8)
         self.k_scale = None if k_scale is None else np.float32(k_scale)
         self.v_scale = None if v_scale is None else np.float32(v_scale)
-        if kind == "e4m3" and (self.k_scale is None or self.v_scale is None):
-            raise ValueError("e4m3 cache needs per-layer k_scale and v_scale")
+        if kind in ("e4m3", "nvfp4") and (self.k_scale is None or self.v_scale is None):
+            raise ValueError("%s cache needs per-layer k_scale and v_scale" % kind)
 
     @property
     def num_slots(self):
@@ -103,6 +116,10 @@ class OracleCache:
         if kind == "e4m3":
             scale = self.k_scale if which == "k" else self.v_scale
             return formats.e4m3_quantize(x32, scale), None
+        if kind == "nvfp4":
+            scale = self.k_scale if which == "k" else self.v_scale
+            q, sc = formats.nvfp4_quantize(x32, scale)
+            return formats.nvfp4_pack(q), sc
         if kind == "bf16":
             b = formats.f32_to_bf16_bits(x32)
             return b.astype("<u2").view(np.uint8).reshape(b.shape[:-1] + (2 * b.shape[-1],)), None
@@ -147,6 +164,10 @@ class OracleCache:
         if kind == "e4m3":
             scale = self.k_scale if which == "k" else self.v_scale
             return formats.e4m3_decode(raw) * np.float64(scale)
+        if kind == "nvfp4":
+            scale = self.k_scale if which == "k" else self.v_scale
+            sc = self.kv_scale[slots, :, 0 if which == "k" else 1]
+            return formats.nvfp4_dequantize(formats.nvfp4_unpack(raw), sc, scale)
         if kind == "bf16":
             bits = np.ascontiguousarray(raw).view("<u2")
             return formats.bf16_bits_to_f32(bits).astype(np.float64)

@@ -157,3 +157,104 @@ def e4m3_calibrate_scale(x):
     """scale = fl32(max|x| / 448) for one tensor (the converter contract)."""
     a = np.max(np.abs(np.asarray(x, dtype=np.float32)))
     return np.float32(a / np.float32(E4M3_MAX))
+
+
+# --------------------------------------------------------------------------
+# NVFP4 rows (a reading; the pages name NVFP4 KV storage as a variant outside
+# the calibrated-E4M3 contract of page "[Model][SM70][FP8] Add calibrated
+# E4M3 QSA KV cache", section "Relationship to vLLM #54846", without its
+# layout): FP4 E2M1 element codes, one E4M3 scale per block of 16
+# consecutive elements of a (token, KV head) row, and one float32 scale per
+# layer and tensor, as the E4M3 cache keeps one per layer.
+#
+# E2M1: 1 sign, 2 exponent (bias 1), 1 mantissa bit; magnitudes 0, 0.5, 1,
+# 1.5, 2, 3, 4, 6; no infinities or NaN.
+# --------------------------------------------------------------------------
+E2M1_MAX = 6.0
+NVFP4_BLOCK = 16
+
+
+def e2m1_decode(codes):
+    """4-bit E2M1 codes (low nibble of each value) -> float64, exactly.
+
+    E >= 1: (-1)^S * 2^(E-1) * (1 + M/2);  E == 0: (-1)^S * M / 2.
+    """
+    c = np.asarray(codes).astype(np.int64) & 0xF
+    sign = np.where(c & 0x8, -1.0, 1.0)
+    e = (c >> 1) & 0x3
+    m = c & 0x1
+    mag = np.where(e == 0, m * 0.5, np.ldexp(1.0 + m / 2.0, (e - 1).astype(np.int64)))
+    return sign * mag
+
+
+def e2m1_encode(y):
+    """float32 -> 4-bit E2M1 codes: nearest magnitude, ties to the even
+    code (mantissa bit 0), saturating at 6 (infinities included); the sign
+    bit is the sign of y (so -0 and small negatives give 0x8); NaN -> 0."""
+    y = np.asarray(y, dtype=np.float32)
+    nan = np.isnan(y)
+    a = np.where(nan, 0.0, np.abs(y.astype(np.float64)))
+    grid = e2m1_decode(np.arange(8))
+    lo = np.clip(np.searchsorted(grid, a, side="right") - 1, 0, 7)
+    hi = np.minimum(lo + 1, 7)
+    dlo = a - grid[lo]
+    dhi = grid[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0) & (hi != lo))
+    code = np.where(a >= E2M1_MAX, 7, np.where(pick_hi, hi, lo)).astype(np.uint8)
+    sign = (np.signbit(y) & ~nan).astype(np.uint8) << np.uint8(3)
+    return code | sign
+
+
+def nvfp4_quantize(x, scale):
+    """Rows of float32 x [..., D] (D a multiple of 16) with the layer's
+    float32 scale g -> (element codes [..., D] 4-bit, block scale codes
+    [..., D/16] E4M3).  Per block of 16: a = max |x| (NaN ignored),
+    s = fl32(a / 6), code = e4m3fn(fl32(s / g)) (round to nearest even,
+    saturating), S = its value; the elements are e2m1(fl32(x / fl32(S g))),
+    or 0 when S g is 0.  Divisions are IEEE float32, as the E4M3 converter's.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    shp = x.shape
+    D = shp[-1]
+    xb = x.reshape(shp[:-1] + (D // NVFP4_BLOCK, NVFP4_BLOCK))
+    with np.errstate(invalid="ignore"):
+        a = np.max(np.where(np.isnan(xb), np.float32(0), np.abs(xb)), axis=-1).astype(np.float32)
+    s = (a / np.float32(E2M1_MAX)).astype(np.float32)
+    with np.errstate(over="ignore"):
+        sc = e4m3_encode((s / np.float32(scale)).astype(np.float32))
+        eff = (e4m3_decode(sc).astype(np.float32) * np.float32(scale)).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        y = (xb / eff[..., None]).astype(np.float32)
+    q = np.where(eff[..., None] > 0, e2m1_encode(y), np.uint8(0))
+    return q.reshape(shp).astype(np.uint8), sc
+
+
+def nvfp4_pack(q):
+    """4-bit codes [..., D] -> bytes [..., D/2]: element 2j in the low nibble
+    of byte j, element 2j + 1 in the high nibble."""
+    q = np.asarray(q, dtype=np.uint8)
+    return (q[..., 0::2] & 0xF) | ((q[..., 1::2] & 0xF) << 4)
+
+
+def nvfp4_unpack(b):
+    b = np.asarray(b, dtype=np.uint8)
+    q = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.uint8)
+    q[..., 0::2] = b & 0xF
+    q[..., 1::2] = b >> 4
+    return q
+
+
+def nvfp4_dequantize(q, sc, scale):
+    """Exact float64 values: e2m1(q) * e4m3(block scale) * g."""
+    v = e2m1_decode(q)
+    S = e4m3_decode(sc)
+    shp = v.shape
+    vb = v.reshape(shp[:-1] + (shp[-1] // NVFP4_BLOCK, NVFP4_BLOCK))
+    return (vb * S[..., None] * np.float64(np.float32(scale))).reshape(shp)
+
+
+def nvfp4_calibrate_scale(x):
+    """g = fl32(max|x| / 2688) for one tensor: the largest block scale,
+    max|x| / 6 / g, lands on E4M3's 448."""
+    a = np.max(np.abs(np.asarray(x, dtype=np.float32)))
+    return np.float32(a / np.float32(E2M1_MAX * E4M3_MAX))
