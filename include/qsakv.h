@@ -91,23 +91,39 @@ typedef enum qkv_dtype {
  *                        and for V (v_scale) ([E4M3-PR] "Purpose";
  *                        [SCALE-PACK] "Calibration").
  * QKV_CACHE_BF16         k, v: bf16 [NB][BS][Hkv][D] (comparison arm).
+ * QKV_CACHE_NVFP4        k, v: FP4 E2M1 codes packed two per byte
+ *                        [NB][BS][Hkv][D/2] (element 2j in the low nibble of
+ *                        byte j); kv_scale: bytes [NB][BS][Hkv][2][D/16] --
+ *                        the E4M3 scale of each 16-element block of the K
+ *                        row, then of the V row; one float32 scale per layer
+ *                        for K (k_scale) and for V (v_scale).  A reading: the
+ *                        pages name NVFP4 KV storage only as a variant
+ *                        outside the E4M3 contract ([E4M3-PR] "Relationship
+ *                        to vLLM #54846").
  *
  * int8 values: per (token, KV head, K|V) row x[0..D): a = max|x_d|,
  * s = fl32(a / 127), q_d = clamp(rne(fl32(x_d / s)), -127, 127); a zero row
  * stores s = 0 and q = 0 ([INT8-PR], "Headline result": per-(token,head)
  * scales).  E4M3 values: code = e4m3fn_satfinite_rne(fl32(x / scale)),
- * reconstructed = code * scale ([SCALE-PACK], "Calibration").
+ * reconstructed = code * scale ([SCALE-PACK], "Calibration").  NVFP4
+ * values, per block of 16 with the layer's scale g: a = max|x| (NaN
+ * ignored), sc = e4m3fn_satfinite_rne(fl32(fl32(a / 6) / g)), S = its value;
+ * element code = e2m1_satfinite_rne(fl32(x / fl32(S * g))) (ties to the
+ * even code, sign kept, NaN -> +0), or 0 when S * g is 0; reconstructed =
+ * e2m1 * S * g.
  */
 typedef enum qkv_cache_kind {
   QKV_CACHE_INT8 = 0,
   QKV_CACHE_INT8_INLINE = 1,
   QKV_CACHE_E4M3 = 2,
-  QKV_CACHE_BF16 = 3
+  QKV_CACHE_BF16 = 3,
+  QKV_CACHE_NVFP4 = 4
 } qkv_cache_kind;
 
 /* One layer's paged cache.  Pointers: device, caller-owned, 16-byte aligned
- * (kv_scale: 8-byte aligned).  k_scale / v_scale: host values, read and
- * validated on every call that uses an E4M3 cache; ignored otherwise. */
+ * (kv_scale: 8-byte aligned for INT8).  k_scale / v_scale: host values,
+ * read and validated on every call that uses an E4M3 or NVFP4 cache;
+ * ignored otherwise. */
 typedef struct qkv_cache {
   int32_t kind;          /* qkv_cache_kind                                 */
   int32_t num_blocks;    /* NB >= 1                                        */
@@ -117,9 +133,9 @@ typedef struct qkv_cache {
   int32_t reserved;      /* must be 0                                      */
   void *k;
   void *v;
-  float *kv_scale;       /* QKV_CACHE_INT8 only                            */
-  float k_scale;         /* QKV_CACHE_E4M3 only                            */
-  float v_scale;         /* QKV_CACHE_E4M3 only                            */
+  float *kv_scale;       /* QKV_CACHE_INT8 (float32), QKV_CACHE_NVFP4 (bytes) */
+  float k_scale;         /* QKV_CACHE_E4M3 and QKV_CACHE_NVFP4             */
+  float v_scale;         /* QKV_CACHE_E4M3 and QKV_CACHE_NVFP4             */
 } qkv_cache;
 
 /* Arguments of one sparse-attention call.
@@ -312,9 +328,9 @@ QSAKV_API qkv_status qsa_topk_select(const void *scores, int32_t score_dtype, in
  * qkv_cache_bytes -- sizes of the k, v and kv_scale tensors of a cache of
  * this kind and shape (scale_bytes = 0 for kinds without a side tensor).
  * Bytes per token, K + V, scales included: INT8 and INT8_INLINE
- * 2*Hkv*(D+4), E4M3 2*Hkv*D, BF16 4*Hkv*D -- 520 vs 1024 at Hkv = 1,
- * D = 256 as in [INT8-CARD] "What it buys you".  Any output pointer may be
- * NULL.
+ * 2*Hkv*(D+4), E4M3 2*Hkv*D, BF16 4*Hkv*D, NVFP4 2*Hkv*(D/2 + D/16) -- 520
+ * vs 1024 at Hkv = 1, D = 256 as in [INT8-CARD] "What it buys you".  Any
+ * output pointer may be NULL.
  */
 QSAKV_API qkv_status qkv_cache_bytes(int32_t kind, int32_t num_blocks, int32_t block_size,
                            int32_t num_kv_heads, int32_t head_dim, size_t *k_bytes,

@@ -66,13 +66,15 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 template <int KIND, int D, int TT>
 struct Geo {
   static_assert(TT == 16, "tiles are 16 tokens: one MFMA block of K rows");
-  static constexpr bool kOneByte = KIND != kBF16;
+  static constexpr bool kOneByte = KIND == kInt8 || KIND == kInt8Inline || KIND == kE4M3;
+  static constexpr bool kFp4 = KIND == kNvfp4;                          // two codes per byte
   static constexpr bool kInt = KIND == kInt8 || KIND == kInt8Inline;
-  static constexpr int kDataBytes = kOneByte ? D : 2 * D;              // K or V row payload
+  static constexpr int kDataBytes = kFp4 ? D / 2 : kOneByte ? D : 2 * D;   // K or V row payload
   static constexpr int kRowBytes = KIND == kInt8Inline ? D + 4 : kDataBytes;
   static constexpr int kKChunks = kDataBytes / 64;                      // 16-B chunks / lane / token
   static constexpr int kVBytes = kDataBytes / 16;                       // bytes / lane / token
   static constexpr int kVWords = kVBytes / 4;
+  static constexpr int kBlkScales = D / 16;                             // NVFP4 block scales / row
   static constexpr int kQK = D / 32;                                    // MFMAs per 16 tokens
   static constexpr int kPV = D / 16;                                    // PV MFMAs per tile
   static constexpr int kOut = D / 4;                                    // outputs per lane
@@ -92,6 +94,9 @@ struct TileRaw {
   u32x4 k[G::kBlk][G::kKChunks];    // tokens 16 b + ln16
   uint32_t v[G::kTok][G::kVWords];  // tokens tok(grp, e)
   float sk[G::kTok], sv[G::kTok];   // int8 scales of tokens tok(grp, e)
+  uint32_t ksc[G::kBlk];            // NVFP4: K block-scale codes of token 16 b + ln16,
+                                    //   byte 2c + i = block 2 grp + 8 c + i
+  uint32_t vsc;                     // NVFP4: byte e = V block-scale code of token tok(grp, e)
   uint32_t valid;                   // bit e: token tok(grp, e) is attended
 };
 
@@ -123,7 +128,17 @@ __device__ __forceinline__ void issue_tile(TileRaw<KIND, D, TT>& t, const AttnPa
         t.k[b][c] = ld<u32x4>(kr + 64 * c);
       }
     }
+    if constexpr (G::kFp4) {
+      // chunk c of this lane holds the codes of blocks 2 grp + 8 c and + 1
+      const uint8_t* sr = reinterpret_cast<const uint8_t*>(p.kv_scale) +
+                          ((int64_t)(s < 0 ? 0 : s) * hkv + g) * 2 * G::kBlkScales + 2 * grp;
+      uint32_t sc = 0;
+#pragma unroll
+      for (int c = 0; c < G::kKChunks; ++c) sc |= (uint32_t)ld<uint16_t>(sr + 8 * c) << (16 * c);
+      t.ksc[b] = sc;
+    }
   }
+  uint32_t vsc = 0;
   int vs[G::kTok];
   {
     const int4 s0 = *reinterpret_cast<const int4*>(ts + 4 * grp);
@@ -148,6 +163,8 @@ __device__ __forceinline__ void issue_tile(TileRaw<KIND, D, TT>& t, const AttnPa
       const u32x2 w = ld<u32x2>(vr);
       t.v[e][0] = w[0];
       t.v[e][1] = w[1];
+    } else if constexpr (G::kVWords == 1) {  // NVFP4, D = 128
+      t.v[e][0] = ld<uint32_t>(vr);
     } else {  // 8 words (bf16, D = 256)
       const u32x4 w0 = ld<u32x4>(vr), w1 = ld<u32x4>(vr + 16);
 #pragma unroll
@@ -162,6 +179,15 @@ __device__ __forceinline__ void issue_tile(TileRaw<KIND, D, TT>& t, const AttnPa
 #pragma unroll
       for (int i = 0; i < G::kVWords; ++i) t.v[e][i] = s < 0 ? 0u : t.v[e][i];
     }
+    if constexpr (G::kFp4) {
+      // the lane's D/16 values of the row form block ln16 * kVBytes / 8; a
+      // padding token's scale is cleared (a NaN scale code stored in row 0
+      // must not reach the weighted sum)
+      const uint8_t* sr = reinterpret_cast<const uint8_t*>(p.kv_scale) +
+                          (rowi * 2 + 1) * G::kBlkScales + ln16 * G::kVBytes / 8;
+      const uint32_t sc = s < 0 ? 0u : (uint32_t)*sr;
+      vsc = e == 0 ? sc : (vsc | (sc << (8 * e)));
+    }
     if constexpr (KIND == kInt8) {
       const float2 sc = *reinterpret_cast<const float2*>(p.kv_scale + rowi * 2);
       t.sk[e] = sc.x;
@@ -172,6 +198,7 @@ __device__ __forceinline__ void issue_tile(TileRaw<KIND, D, TT>& t, const AttnPa
     }
   }
   t.valid = valid;
+  if constexpr (G::kFp4) t.vsc = vsc;
 }
 
 struct WaveState {
@@ -238,6 +265,18 @@ __device__ __forceinline__ void compute_tile(const TileRaw<KIND, D, TT>& t, cons
     for (int i = 0; i < G::kQK; ++i) {
       if constexpr (KIND == kBF16) {
         s[b] = mfma16(bitcast<bf16x8>(t.k[b][i]), q[i], s[b]);
+      } else if constexpr (G::kFp4) {
+        // step i: word i & 3 of chunk i >> 2 (8 codes), block 2 grp + 8 (i >> 2)
+        // + ((i & 3) >> 1); operand = E2M1 value x block scale, exact in fp16
+        const uint32_t w = t.k[b][i >> 2][i & 3];
+        const uint32_t scb = (t.ksc[b] >> (16 * (i >> 2) + 8 * ((i & 3) >> 1))) & 0xFFu;
+        const f16x2 sc2 = bitcast<f16x2>(e4m3pair_to_f16x2<false>(scb | (scb << 8)));
+        u32x4 a;
+        a[0] = bitcast<uint32_t>(bitcast<f16x2>(e2m1pair_to_f16x2<0>(w)) * sc2);
+        a[1] = bitcast<uint32_t>(bitcast<f16x2>(e2m1pair_to_f16x2<1>(w)) * sc2);
+        a[2] = bitcast<uint32_t>(bitcast<f16x2>(e2m1pair_to_f16x2<2>(w)) * sc2);
+        a[3] = bitcast<uint32_t>(bitcast<f16x2>(e2m1pair_to_f16x2<3>(w)) * sc2);
+        s[b] = mfma16(bitcast<f16x8>(a), q[i], s[b]);
       } else {
         const u32x4& c = t.k[b][i >> 1];
         const uint32_t w0 = c[2 * (i & 1)], w1 = c[2 * (i & 1) + 1];
@@ -332,6 +371,45 @@ __device__ __forceinline__ void compute_tile(const TileRaw<KIND, D, TT>& t, cons
         a[1] = perm(t.v[3][c], t.v[2][c], sel);
         o[2 * c + hb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bitcast<bf16x4>(a), bw,
                                                                    o[2 * c + hb], 0, 0, 0);
+      }
+    }
+  } else if constexpr (G::kFp4) {
+    // token e's word c: 8 codes = the lane's d-values 8 c .. 8 c + 7, times
+    // the token's block scale (exact in fp16); the A operand of d-value dd
+    // gathers the four tokens' halves
+    f16x4 bw;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bw[e] = (_Float16)w[e];
+    f16x2 sc2[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t scb = (t.vsc >> (8 * e)) & 0xFFu;
+      sc2[e] = bitcast<f16x2>(e4m3pair_to_f16x2<false>(scb | (scb << 8)));
+    }
+#pragma unroll
+    for (int c = 0; c < G::kVWords; ++c) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t r[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          uint32_t pr;
+          const uint32_t wv = t.v[e][c];
+          if (j == 0) pr = e2m1pair_to_f16x2<0>(wv);
+          else if (j == 1) pr = e2m1pair_to_f16x2<1>(wv);
+          else if (j == 2) pr = e2m1pair_to_f16x2<2>(wv);
+          else pr = e2m1pair_to_f16x2<3>(wv);
+          r[e] = bitcast<uint32_t>(bitcast<f16x2>(pr) * sc2[e]);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t sel = h ? 0x07060302u : 0x05040100u;
+          u32x2 a;
+          a[0] = perm(r[1], r[0], sel);
+          a[1] = perm(r[3], r[2], sel);
+          o[8 * c + 2 * j + h] = __builtin_amdgcn_mfma_f32_16x16x16f16(bitcast<f16x4>(a), bw,
+                                                                      o[8 * c + 2 * j + h], 0, 0, 0);
+        }
       }
     }
   } else {
@@ -439,7 +517,8 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
     const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + qoff;
 #pragma unroll
     for (int i = 0; i < G::kQK; ++i) {
-      const int d0 = G::kOneByte ? 64 * (i >> 1) + 16 * grp + 8 * (i & 1) : 32 * i + 8 * grp;
+      const int d0 = G::kFp4 ? 128 * (i >> 2) + 32 * grp + 8 * (i & 3)
+                   : G::kOneByte ? 64 * (i >> 1) + 16 * grp + 8 * (i & 1) : 32 * i + 8 * grp;
       qraw[i] = head_ok ? *reinterpret_cast<const u32x4*>(qrow + d0) : u32x4{0, 0, 0, 0};
     }
   }
@@ -755,6 +834,7 @@ hipError_t launch_attn(int kind, int head_dim, const AttnParams& p, hipStream_t 
     case kInt8: return launch_kind<kInt8>(head_dim, p, s);
     case kInt8Inline: return launch_kind<kInt8Inline>(head_dim, p, s);
     case kE4M3: return launch_kind<kE4M3>(head_dim, p, s);
+    case kNvfp4: return launch_kind<kNvfp4>(head_dim, p, s);
     default: return launch_kind<kBF16>(head_dim, p, s);
   }
 }

@@ -7,7 +7,11 @@
 // q = clamp(rne(fl32(x / s)), -127, 127), a zero row stores s = 0, q = 0.
 // The E4M3 rule is the converter contract of page "Qwen3.8 Flash Next NVFP4
 // QSA FP8 E4M3 KV Scales" (section "Calibration"):
-// code = e4m3fn(fl32(x / scale)) with saturation.  Both quotients are IEEE
+// code = e4m3fn(fl32(x / scale)) with saturation.  NVFP4 (a reading: the
+// pages name it only as a KV variant outside that contract): per block of
+// 16 elements -- exactly a lane's share -- a = max|x|, block scale code
+// sc = e4m3fn(fl32(fl32(a / 6) / g)) with the layer's scale g, and element
+// codes e2m1(fl32(x / fl32(S g))), S the value of sc.  All quotients are IEEE
 // correctly rounded fp32 divisions (hipcc's default '/'), so every stored
 // byte is determined by its source row alone and is bit-exact.
 #include "qsakv_device.h"
@@ -82,6 +86,24 @@ __device__ __forceinline__ uint32_t e4m3_encode(float y) {
   return sign | code;
 }
 
+// E4M3FN code (0 .. 0x7E, sign clear) -> its value, exactly.
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const int e = (int)((c >> 3) & 0xFu), m = (int)(c & 7u);
+  return e ? ldexpf((float)(8 + m), e - 10) : ldexpf((float)m, -9);
+}
+
+// FP4 E2M1 code of an fp32 value: the nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6
+// with ties to the even code (the midpoints 0.25, 0.75, 1.25, 1.75, 2.5,
+// 3.5, 5 go to codes 0, 2, 2, 4, 4, 6, 6), saturating at 6; sign bit from
+// y; NaN -> +0.
+__device__ __forceinline__ uint32_t e2m1_encode(float y) {
+  const float a = fabsf(y);
+  if (!(a == a)) return 0u;
+  const uint32_t c = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+                   : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.0f ? 6u : 7u;
+  return ((__float_as_uint(y) >> 28) & 8u) | c;
+}
+
 template <int KIND, int D, int SRC>
 __global__ __launch_bounds__(kWavesPerBlock * kWave) void kv_write_kernel(WriteParams p) {
   constexpr int kLPR = D / kEPL;         // lanes per row
@@ -134,6 +156,23 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void kv_write_kernel(WriteP
 #pragma unroll
       for (int i = 0; i < kEPL; ++i) w[i >> 2] |= e4m3_encode(x[i] / scale) << (8 * (i & 3));
       *reinterpret_cast<u32x4*>(base + row * D + part * kEPL) = u32x4{w[0], w[1], w[2], w[3]};
+    } else if constexpr (KIND == kNvfp4) {
+      const float g = which ? p.v_scale : p.k_scale;
+      float a = 0.f;
+#pragma unroll
+      for (int i = 0; i < kEPL; ++i) {   // NaN ignored: a comparison with NaN is false
+        const float v = fabsf(x[i]);     // (a NaN-quieting max could pass a NaN on)
+        a = v > a ? v : a;
+      }
+      const float sb = a / 6.0f;
+      const uint32_t sc = e4m3_encode(sb / g);
+      const float eff = e4m3_value(sc) * g;
+      uint32_t w[2] = {0u, 0u};
+#pragma unroll
+      for (int i = 0; i < kEPL; ++i)
+        w[i >> 3] |= (eff > 0.f ? e2m1_encode(x[i] / eff) : 0u) << (4 * (i & 7));
+      *reinterpret_cast<u32x2*>(base + row * (D / 2) + part * 8) = u32x2{w[0], w[1]};
+      reinterpret_cast<uint8_t*>(p.kv_scale)[(row * 2 + which) * (D / 16) + part] = (uint8_t)sc;
     } else {  // kBF16: round to nearest even (identity for bf16 sources)
       uint32_t w[8];
 #pragma unroll
@@ -177,6 +216,7 @@ hipError_t launch_kv_write(int kind, int head_dim, const WriteParams& p, hipStre
     case kInt8: return launch_d<kInt8>(head_dim, p, s);
     case kInt8Inline: return launch_d<kInt8Inline>(head_dim, p, s);
     case kE4M3: return launch_d<kE4M3>(head_dim, p, s);
+    case kNvfp4: return launch_d<kNvfp4>(head_dim, p, s);
     default: return launch_d<kBF16>(head_dim, p, s);
   }
 }

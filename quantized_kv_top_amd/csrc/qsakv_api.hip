@@ -69,6 +69,7 @@ int64_t row_bytes(int kind, int64_t d) {
     case QKV_CACHE_INT8: return d;
     case QKV_CACHE_INT8_INLINE: return d + 4;
     case QKV_CACHE_E4M3: return d;
+    case QKV_CACHE_NVFP4: return d / 2;
     default: return 2 * d;
   }
 }
@@ -76,7 +77,7 @@ int64_t row_bytes(int kind, int64_t d) {
 // Checks shared by every call that touches a cache.
 qkv_status check_cache(const qkv_cache* c, bool need_data) {
   if (!c) return QKV_ERR_NULL;
-  if (c->kind < QKV_CACHE_INT8 || c->kind > QKV_CACHE_BF16) return QKV_ERR_UNSUPPORTED;
+  if (c->kind < QKV_CACHE_INT8 || c->kind > QKV_CACHE_NVFP4) return QKV_ERR_UNSUPPORTED;
   if (c->num_blocks <= 0 || c->num_kv_heads <= 0 || c->reserved != 0) return QKV_ERR_BAD_SHAPE;
   if (!is_pow2(c->block_size) || c->block_size > 1024) return QKV_ERR_BAD_SHAPE;
   if (c->head_dim != 128 && c->head_dim != 256) return QKV_ERR_UNSUPPORTED;
@@ -86,12 +87,14 @@ qkv_status check_cache(const qkv_cache* c, bool need_data) {
     return QKV_ERR_BAD_SHAPE;
   if (need_data) {
     if (!c->k || !c->v) return QKV_ERR_NULL;
-    if (c->kind == QKV_CACHE_INT8 && !c->kv_scale) return QKV_ERR_NULL;
+    const bool side = c->kind == QKV_CACHE_INT8 || c->kind == QKV_CACHE_NVFP4;
+    if (side && !c->kv_scale) return QKV_ERR_NULL;
     const uintptr_t a = c->kind == QKV_CACHE_INT8_INLINE ? 4 : 16;
     if (!aligned(c->k, a) || !aligned(c->v, a)) return QKV_ERR_ALIGNMENT;
-    if (c->kind == QKV_CACHE_INT8 && !aligned(c->kv_scale, 8)) return QKV_ERR_ALIGNMENT;
+    if (side && !aligned(c->kv_scale, c->kind == QKV_CACHE_INT8 ? 8 : 16)) return QKV_ERR_ALIGNMENT;
   }
-  if (c->kind == QKV_CACHE_E4M3 && (!scale_ok(c->k_scale) || !scale_ok(c->v_scale)))
+  if ((c->kind == QKV_CACHE_E4M3 || c->kind == QKV_CACHE_NVFP4) &&
+      (!scale_ok(c->k_scale) || !scale_ok(c->v_scale)))
     return QKV_ERR_BAD_SCALE;
   return QKV_OK;
 }
@@ -142,8 +145,9 @@ qsakv::AttnParams make_params(const qkv_cache* c, const qsa_args* a, int32_t spl
   p.v = static_cast<const uint8_t*>(c->v);
   p.kv_scale = c->kv_scale;
   p.sm_log2e = (float)((double)a->sm_scale * 1.4426950408889634);
-  p.k_scale = c->kind == QKV_CACHE_E4M3 ? c->k_scale : 1.f;
-  p.v_scale = c->kind == QKV_CACHE_E4M3 ? c->v_scale : 1.f;
+  const bool layer_scales = c->kind == QKV_CACHE_E4M3 || c->kind == QKV_CACHE_NVFP4;
+  p.k_scale = layer_scales ? c->k_scale : 1.f;
+  p.v_scale = layer_scales ? c->v_scale : 1.f;
   p.q_dtype = a->q_dtype;
   p.out_dtype = a->out_dtype;
   p.num_rows = a->num_rows;
@@ -349,7 +353,7 @@ qkv_status qsa_topk_select(const void* scores, int32_t score_dtype, int32_t num_
 qkv_status qkv_cache_bytes(int32_t kind, int32_t num_blocks, int32_t block_size,
                            int32_t num_kv_heads, int32_t head_dim, size_t* k_bytes,
                            size_t* v_bytes, size_t* scale_bytes) {
-  if (kind < QKV_CACHE_INT8 || kind > QKV_CACHE_BF16) return QKV_ERR_UNSUPPORTED;
+  if (kind < QKV_CACHE_INT8 || kind > QKV_CACHE_NVFP4) return QKV_ERR_UNSUPPORTED;
   if (head_dim != 128 && head_dim != 256) return QKV_ERR_UNSUPPORTED;
   if (num_blocks <= 0 || num_kv_heads <= 0 || !is_pow2(block_size) || block_size > 1024)
     return QKV_ERR_BAD_SHAPE;
@@ -358,6 +362,7 @@ qkv_status qkv_cache_bytes(int32_t kind, int32_t num_blocks, int32_t block_size,
       !mul_ok(rows, row_bytes(kind, head_dim), &kb))
     return QKV_ERR_BAD_SHAPE;
   if (kind == QKV_CACHE_INT8 && !mul_ok(rows, 8, &sb)) return QKV_ERR_BAD_SHAPE;
+  if (kind == QKV_CACHE_NVFP4 && !mul_ok(rows, 2 * (head_dim / 16), &sb)) return QKV_ERR_BAD_SHAPE;
   if (k_bytes) *k_bytes = (size_t)kb;
   if (v_bytes) *v_bytes = (size_t)kb;
   if (scale_bytes) *scale_bytes = (size_t)sb;

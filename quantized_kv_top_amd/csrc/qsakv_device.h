@@ -88,6 +88,14 @@ __device__ __forceinline__ uint32_t e4m3pair_to_f16x2(uint32_t w) {
   f16x2 h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, kHiWord);
   return bitcast<uint32_t>(h);
 }
+// The two FP4 E2M1 codes in byte kByte of w -> the fp16 pair (low nibble,
+// high nibble): gfx950's FP4 conversion with unit scale (exact: every E2M1
+// value is an fp16 value).
+template <int kByte>
+__device__ __forceinline__ uint32_t e2m1pair_to_f16x2(uint32_t w) {
+  f16x2 h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, kByte);
+  return bitcast<uint32_t>(h);
+}
 // ---------------------------------------------------------------------------
 // MFMA 16x16x32 (fp16 / bf16 inputs, fp32 accumulate)
 //   A (16 x 32): lane l holds row l%16, k-slots 8*(l/16) .. +7

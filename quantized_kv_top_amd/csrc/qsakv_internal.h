@@ -8,7 +8,7 @@
 
 namespace qsakv {
 
-enum Kind : int { kInt8 = 0, kInt8Inline = 1, kE4M3 = 2, kBF16 = 3 };
+enum Kind : int { kInt8 = 0, kInt8Inline = 1, kE4M3 = 2, kBF16 = 3, kNvfp4 = 4 };
 enum DType : int { kDtBF16 = 0, kDtFP16 = 1, kDtFP32 = 2 };
 
 // Everything a write kernel needs; validated by the caller.
@@ -18,8 +18,8 @@ struct WriteParams {
   const int64_t* slot_mapping;
   uint8_t* k;
   uint8_t* v;
-  float* kv_scale;
-  float k_scale;          // E4M3 only
+  float* kv_scale;        // INT8: float32 (K, V) per row; NVFP4: block-scale bytes
+  float k_scale;          // E4M3 and NVFP4 per-layer scales
   float v_scale;
   int64_t num_tokens;
   int64_t num_slots;      // NB * BS
@@ -73,11 +73,11 @@ struct AttnParams {
   float* lse;             // may be null
   const uint8_t* k;
   const uint8_t* v;
-  const float* kv_scale;  // INT8 side layout
+  const float* kv_scale;  // INT8 side layout; NVFP4 block-scale bytes
   float* ws_o;            // split-K partials [R][Hq][P][D]   (P > 1)
   float* ws_ml;           // split-K (max, sum) [R][Hq][P][2] (P > 1)
   float sm_log2e;         // sm_scale * log2(e)
-  float k_scale;          // E4M3 per-layer scales (1 otherwise)
+  float k_scale;          // E4M3 / NVFP4 per-layer scales (1 otherwise)
   float v_scale;
   int32_t q_dtype;
   int32_t out_dtype;

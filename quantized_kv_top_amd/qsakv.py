@@ -19,9 +19,9 @@ OK, ERR_NULL, ERR_BAD_SHAPE, ERR_UNSUPPORTED, ERR_BAD_SCALE, ERR_WORKSPACE, ERR_
 # dtypes (qkv_dtype)
 BF16, FP16, FP32 = 0, 1, 2
 # cache kinds (qkv_cache_kind)
-CACHE_INT8, CACHE_INT8_INLINE, CACHE_E4M3, CACHE_BF16 = 0, 1, 2, 3
+CACHE_INT8, CACHE_INT8_INLINE, CACHE_E4M3, CACHE_BF16, CACHE_NVFP4 = 0, 1, 2, 3, 4
 KIND_BY_NAME = {"int8": CACHE_INT8, "int8_inline": CACHE_INT8_INLINE,
-                "e4m3": CACHE_E4M3, "bf16": CACHE_BF16}
+                "e4m3": CACHE_E4M3, "bf16": CACHE_BF16, "nvfp4": CACHE_NVFP4}
 
 EXPORTED = ("kv_quant_write", "qsa_sparse_attn_prefill", "qsa_decode_workspace_bytes",
             "qsa_sparse_attn_decode", "qkv_calib_workspace_bytes", "kv_calib_stats",
@@ -142,8 +142,9 @@ class Cache:
     """One layer's paged cache: device tensors plus the descriptor.
 
     ``k``/``v`` are uint8 tensors of the layout's bytes; ``kv_scale`` is the
-    float32 side tensor (int8 kind) or None; ``k_scale``/``v_scale`` are the
-    per-layer E4M3 scales (host floats).
+    side tensor -- float32 row scales (int8), uint8 block-scale codes
+    (nvfp4) -- or None; ``k_scale``/``v_scale`` are the per-layer E4M3 /
+    NVFP4 scales (host floats).
     """
 
     def __init__(self, kind, num_blocks, block_size, num_kv_heads, head_dim, device="cuda",
@@ -156,7 +157,12 @@ class Cache:
         alloc = torch.zeros if zero else torch.empty
         self.k = alloc(kb, dtype=torch.uint8, device=device)
         self.v = alloc(vb, dtype=torch.uint8, device=device)
-        self.kv_scale = alloc(sb // 4, dtype=torch.float32, device=device) if sb else None
+        if not sb:
+            self.kv_scale = None
+        elif kind == "nvfp4":
+            self.kv_scale = alloc(sb, dtype=torch.uint8, device=device)
+        else:
+            self.kv_scale = alloc(sb // 4, dtype=torch.float32, device=device)
         self.k_scale = float(k_scale)
         self.v_scale = float(v_scale)
 
@@ -172,7 +178,8 @@ class Cache:
 
     def nbytes(self):
         return self.k.numel() + self.v.numel() + (0 if self.kv_scale is None else
-                                                  4 * self.kv_scale.numel())
+                                                  self.kv_scale.numel() *
+                                                  self.kv_scale.element_size())
 
 
 def kv_quant_write(cache, k_src, v_src, slot_mapping, stream=None):

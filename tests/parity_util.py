@@ -37,6 +37,23 @@ def e4m3_scales(w):
             float(ofmt.e4m3_calibrate_scale(np.array([va], np.float32))))
 
 
+def nvfp4_scales(w):
+    """Per-layer K and V scales of an NVFP4 cache: max|x| / (6 * 448)."""
+    ka = np.float32(w.k_src.abs().max().float().item())
+    va = np.float32(w.v_src.abs().max().float().item())
+    return (float(ofmt.nvfp4_calibrate_scale(np.array([ka], np.float32))),
+            float(ofmt.nvfp4_calibrate_scale(np.array([va], np.float32))))
+
+
+def layer_scales(kind, w):
+    """(k_scale, v_scale) for kinds with per-layer scales, else (None, None)."""
+    if kind == "e4m3":
+        return e4m3_scales(w)
+    if kind == "nvfp4":
+        return nvfp4_scales(w)
+    return None, None
+
+
 def gpu_write(kind, w, k_scale=1.0, v_scale=1.0, num_blocks=None):
     c = qsakv.Cache(kind, num_blocks or w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim,
                     k_scale=k_scale, v_scale=v_scale)
@@ -68,7 +85,10 @@ def gpu_rows(c, slots):
     s = dev(np.asarray(slots, np.int64))
     k = c.k.view(c.num_slots, H, rb)[s].cpu().numpy()
     v = c.v.view(c.num_slots, H, rb)[s].cpu().numpy()
-    sc = None if c.kv_scale is None else c.kv_scale.view(c.num_slots, H, 2)[s].cpu().numpy()
+    sc = None
+    if c.kv_scale is not None:
+        per = c.kv_scale.numel() // (c.num_slots * H)
+        sc = c.kv_scale.view(c.num_slots, H, per)[s].cpu().numpy()
     return k, v, sc
 
 
@@ -78,7 +98,11 @@ def assert_rows_equal(c, oc, slots):
     np.testing.assert_array_equal(k, oc.k[slots])
     np.testing.assert_array_equal(v, oc.v[slots])
     if sc is not None:
-        np.testing.assert_array_equal(sc.view(np.uint32), oc.kv_scale[slots].view(np.uint32))
+        want = oc.kv_scale[slots]
+        if want.dtype == np.float32:
+            np.testing.assert_array_equal(sc.view(np.uint32), want.view(np.uint32))
+        else:                                   # block-scale bytes [n][H][2][D/16]
+            np.testing.assert_array_equal(sc, want.reshape(sc.shape))
 
 
 def run_attention(c, w, num_splits=1, out_dtype=None, lse=True, decode=None, topk_idx=None,

@@ -9,16 +9,16 @@ from oracle import formats as ofmt
 from quantized_kv_top_amd import qsakv
 from quantized_kv_top_amd import workloads as wl
 
-from parity_util import (check, dev, e4m3_scales, gpu_write, oracle_attention, oracle_write,
-                         run_attention, say)
+from parity_util import (check, dev, e4m3_scales, gpu_write, layer_scales, oracle_attention,
+                         oracle_write, run_attention, say)
 
 pytestmark = pytest.mark.gpu
 
-KINDS = ["int8", "int8_inline", "e4m3", "bf16"]
+KINDS = ["int8", "int8_inline", "e4m3", "bf16", "nvfp4"]
 
 
 def _setup(kind, w):
-    ks, vs = e4m3_scales(w) if kind == "e4m3" else (None, None)
+    ks, vs = layer_scales(kind, w)
     c = gpu_write(kind, w, ks or 1.0, vs or 1.0)
     oc = oracle_write(kind, w, ks, vs)
     return c, oc
@@ -73,7 +73,7 @@ def test_small_multitile(kind, D):
         check(o, l, ro, rl, "small %s D%d %s" % (kind, D, od))
 
 
-@pytest.mark.parametrize("kind", ["int8", "int8_inline", "e4m3"])
+@pytest.mark.parametrize("kind", ["int8", "int8_inline", "e4m3", "nvfp4"])
 def test_fp16_queries(kind):
     w = small_workload(seed=11, q_dtype="fp16", src="fp16", D=128, Hq=32, Hkv=4, topk=77)
     c, oc = _setup(kind, w)
@@ -258,6 +258,36 @@ def test_every_e4m3_code_decodes_exactly():
     got = out.cpu().numpy()
     assert np.array_equal(got, np.repeat(want[:, None, None], D, axis=2).astype(np.float32))
     assert np.all(lse.cpu().numpy() == 0)
+
+
+@pytest.mark.parametrize("D", [128, 256])
+def test_every_fp4_byte_decodes_exactly(D):
+    """V rows holding every byte value (two E2M1 codes) with every V block
+    scaled by a different E4M3 code; read back with top-k = 1: out =
+    e2m1(code) * block scale * v_scale exactly (element 2j from the low
+    nibble of byte j)."""
+    Hkv, BS = 1, 16
+    n = 256
+    NB = -(-n // BS)
+    c = qsakv.Cache("nvfp4", NB, BS, Hkv, D, k_scale=1.0, v_scale=0.375)
+    rng = np.random.default_rng(3)
+    vbytes = np.stack([np.roll(np.arange(256, dtype=np.uint8), r)[:D // 2] for r in range(n)])
+    c.v.view(NB * BS, D // 2)[:n] = dev(vbytes)
+    nb = D // 16
+    scodes = rng.integers(1, 0x7F, size=(n, nb)).astype(np.uint8)      # finite, positive
+    sc = np.zeros((NB * BS, 2, nb), np.uint8)
+    sc[:n, 1] = scodes
+    sc[:n, 0] = 0x38                                                     # K blocks: 1.0
+    c.kv_scale.copy_(dev(sc.reshape(-1)))
+    q = torch.zeros(n, 1, D, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty(n, 1, D, dtype=torch.float32, device="cuda")
+    bt = dev(np.arange(NB, dtype=np.int32)[None], torch.int32)
+    idx = dev(np.arange(n, dtype=np.int32)[:, None], torch.int32)
+    rs = torch.zeros(n, dtype=torch.int32, device="cuda")
+    qsakv.qsa_sparse_attn_prefill(c, q, rs, bt, idx, 0.1, out)
+    torch.cuda.synchronize()
+    want = ofmt.nvfp4_dequantize(ofmt.nvfp4_unpack(vbytes), scodes, 0.375)
+    np.testing.assert_array_equal(out.cpu().numpy()[:, 0], want.astype(np.float32))
 
 
 def test_every_int8_code_decodes_exactly():

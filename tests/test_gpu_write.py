@@ -11,15 +11,15 @@ from oracle import formats as ofmt
 from quantized_kv_top_amd import qsakv
 from quantized_kv_top_amd import workloads as wl
 
-from parity_util import assert_rows_equal, dev, e4m3_scales, gpu_write, oracle_write, say
+from parity_util import assert_rows_equal, dev, gpu_write, layer_scales, oracle_write, say
 
 pytestmark = pytest.mark.gpu
 
-KINDS = ["int8", "int8_inline", "e4m3", "bf16"]
+KINDS = ["int8", "int8_inline", "e4m3", "bf16", "nvfp4"]
 
 
 def _scales(kind, w):
-    return e4m3_scales(w) if kind == "e4m3" else (None, None)
+    return layer_scales(kind, w)
 
 
 @pytest.mark.parametrize("kind", KINDS)
@@ -80,7 +80,8 @@ def test_write_dtypes_and_special_rows(kind, D, src):
     w = wl.Workload("t", 2 * H, H, D, BS, NB, "bf16", "fp32", src, kt, vt, slots,
                     torch.zeros(1, 2 * H, D, dtype=torch.bfloat16), np.zeros(1, np.int32),
                     np.zeros((1, 1), np.int32), np.zeros((1, 1), np.int32), 0.1)
-    ks, vs = (0.0171247218, 0.0841238871) if kind == "e4m3" else (None, None)
+    ks, vs = {"e4m3": (0.0171247218, 0.0841238871),
+              "nvfp4": (0.0021, 0.0000317)}.get(kind, (None, None))
     say("write", kind, D, src)
     c = gpu_write(kind, w, ks or 1.0, vs or 1.0)
     good = (slots >= 0) & (slots < NB * BS)
@@ -123,6 +124,40 @@ def test_e4m3_encoder_bit_sweep(scale):
     nan = np.isnan(x.ravel())
     np.testing.assert_array_equal(got[~nan], want[~nan])
     assert np.all(got[nan] & 0x7F == 0x7F)
+
+
+@pytest.mark.parametrize("g", [1.0, 0.0021, 3.0e-6])
+def test_nvfp4_blocks_sweep(g):
+    """NVFP4 rows whose blocks hold the fp32 sweep values (NaN, +-inf,
+    subnormals, every exponent) and blocks built on the E2M1 midpoints of a
+    representable block scale (ties): element codes and block-scale codes
+    must equal the oracle's."""
+    vals = _sweep_values()
+    D, H = 256, 1
+    rng = np.random.default_rng(17)
+    T0 = vals.size // D
+    x = vals[:T0 * D].reshape(T0, D).copy()
+    # tie rows: midpoints between E2M1 values times S g, with S = 2.5 (E4M3
+    # exact) and the block max 6 S g so that the block scale is exactly S
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0], np.float32)
+    tie = np.empty((64, D), np.float32)
+    for r in range(64):
+        m = rng.choice(mids, size=D) * np.where(rng.random(D) < 0.5, -1, 1)
+        m[::16] = 6.0
+        tie[r] = (m * np.float32(2.5) * np.float32(g)).astype(np.float32)
+    x = np.concatenate([x, tie])
+    T = x.shape[0]
+    kt = torch.from_numpy(x.reshape(T, H, D).copy())
+    BS = 64
+    NB = -(-T // BS)
+    slots = np.arange(T, dtype=np.int64)
+    w = wl.Workload("nvfp4 sweep", 1, 1, D, BS, NB, "bf16", "fp32", "fp32", kt, kt, slots,
+                    torch.zeros(1, 1, D, dtype=torch.bfloat16), np.zeros(1, np.int32),
+                    np.zeros((1, 1), np.int32), np.zeros((1, 1), np.int32), 0.1)
+    say("nvfp4 sweep g", g, "rows", T)
+    c = gpu_write("nvfp4", w, g, g)
+    oc = oracle_write("nvfp4", w, g, g)
+    assert_rows_equal(c, oc, np.arange(T))
 
 
 def test_write_is_deterministic_and_launch_independent():

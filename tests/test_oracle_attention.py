@@ -89,9 +89,9 @@ def _single_seq(kind, ctx, Hq, Hkv, D, BS, k, v, seed=0):
     nb = ctx // BS
     bt = rng.permutation(nb).reshape(1, nb).astype(np.int32)
     slots = wl.slot_mapping_for(bt, 0, np.arange(ctx), BS)
+    cal = {"e4m3": formats.e4m3_calibrate_scale, "nvfp4": formats.nvfp4_calibrate_scale}.get(kind)
     c = cache.OracleCache(kind, nb, BS, Hkv, D,
-                          *( (formats.e4m3_calibrate_scale(k), formats.e4m3_calibrate_scale(v))
-                             if kind == "e4m3" else (None, None)))
+                          *((cal(k), cal(v)) if cal else (None, None)))
     c.write(k, v, "fp32", slots)
     return c, bt
 
