@@ -56,8 +56,10 @@ def source_sha():
 
 def gathered_bytes_per_row(kind, topk, hkv, d):
     """Algorithmic gathered-KV bytes per query row: every listed token's K and
-    V row of every KV head, plus its int8 scales (4 B each)."""
-    per = {"int8": 2 * (d + 4), "int8_inline": 2 * (d + 4), "e4m3": 2 * d, "bf16": 4 * d}[kind]
+    V row of every KV head, plus its int8 scales (4 B each) or NVFP4 block
+    scales (1 B per 16 elements)."""
+    per = {"int8": 2 * (d + 4), "int8_inline": 2 * (d + 4), "e4m3": 2 * d, "bf16": 4 * d,
+           "nvfp4": 2 * (d // 2 + d // 16)}[kind]
     return topk * hkv * per
 
 
@@ -278,24 +280,37 @@ def graph_loop(layers, steps, warmup, reps):
     return total, per
 
 
+def layer_scales(kind, k_src, v_src):
+    """Per-layer (k_scale, v_scale): max|x| / 448 (E4M3), max|x| / (6 * 448)
+    (NVFP4), 1 otherwise."""
+    if kind not in ("e4m3", "nvfp4"):
+        return 1.0, 1.0
+    d = np.float32(448.0 if kind == "e4m3" else 6.0 * 448.0)
+    return tuple(float(np.float32(t.abs().max().float().item()) / d) for t in (k_src, v_src))
+
+
 def bench_decode(args):
     L = args.layers or 8
-    log("building %d decode layers (8 x 128K tokens each)" % L)
-    layers = [DecodeLayer(wl.decode(device="cuda", seed=200 + i), "int8") for i in range(L)]
+    kind = args.kind or "int8"
+    log("building %d decode layers (8 x 128K tokens each, %s)" % (L, kind))
+    layers = []
+    for i in range(L):
+        w = wl.decode(device="cuda", seed=200 + i)
+        layers.append(DecodeLayer(w, kind, *layer_scales(kind, w.k_src, w.v_src)))
     torch.cuda.synchronize()
     total, per = graph_loop(layers, args.steps, args.warmup, 1)
     calls = args.steps * L
     ms_call = total / calls
     w = layers[0].w
     rows = w.num_rows
-    b = rows * gathered_bytes_per_row("int8", w.topk, 2, 256)
+    b = rows * gathered_bytes_per_row(kind, w.topk, 2, 256)
     return {"metric": METRIC, "value": rows / (ms_call / 1e3), "unit": "rows/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_call,
-            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": kind,
             "data": "synthetic",
             "config": {"workload": "decode: 8 seqs x 128K ctx, 5 rows each (40), top-k 2048 "
-                                   "(70%% recent window), split-K 8 + merge, int8 side scales; "
-                                   "%d layers rotated, graph-captured" % L,
+                                   "(70%% recent window), split-K 8 + merge, %s cache; "
+                                   "%d layers rotated, graph-captured" % (kind, L),
                        "gathered_kv_bytes_per_call": b,
                        "gathered_kv_GBps": b / (ms_call / 1e3) / 1e9,
                        "hbm_frac": b / (ms_call / 1e3) / 1e9 / HBM_PEAK_GBPS}}
@@ -305,26 +320,25 @@ def bench_e4m3(args):
     L = 12
     sets = args.layers or 4        # independent caches per layer position
     splits = args.splits
-    log("building %d x %d E4M3 layers" % (L, sets))
+    kind = args.kind or "e4m3"     # nvfp4: the same 12-layer shape in NVFP4 caches
+    log("building %d x %d %s layers" % (L, sets, kind))
     layers = []
     for s in range(sets):
         for layer in range(L):
             w = wl.e4m3_layer(layer, device="cuda", seed=4 + 1000 * s)
-            ks = float(np.float32(w.k_src.abs().max().float().item()) / np.float32(448))
-            vs = float(np.float32(w.v_src.abs().max().float().item()) / np.float32(448))
-            layers.append(DecodeLayer(w, "e4m3", ks, vs, splits))
+            layers.append(DecodeLayer(w, kind, *layer_scales(kind, w.k_src, w.v_src), splits))
     torch.cuda.synchronize()
     total, per = graph_loop(layers, args.steps, args.warmup, 1)
     ms_step = total / args.steps / sets          # one 12-layer step
     w = layers[0].w
-    b = L * w.num_rows * gathered_bytes_per_row("e4m3", w.topk, 4, 128)
+    b = L * w.num_rows * gathered_bytes_per_row(kind, w.topk, 4, 128)
     return {"metric": METRIC, "value": L * w.num_rows / (ms_step / 1e3),
             "unit": "layer-rows/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
-            "vs_baseline": None, "dtype": "e4m3", "data": "synthetic",
-            "config": {"workload": "e4m3: 12 layers x 4 rows, top-k 2051, Hq 32 / Hkv 4, D 128, "
+            "vs_baseline": None, "dtype": kind, "data": "synthetic",
+            "config": {"workload": "%s: 12 layers x 4 rows, top-k 2051, Hq 32 / Hkv 4, D 128, "
                                    "split-K %d; %d independent 12-layer sets rotated, "
-                                   "graph-captured" % (splits, sets),
+                                   "graph-captured" % (kind, splits, sets),
                        "gathered_kv_bytes_per_step": b,
                        "gathered_kv_GBps": b / (ms_step / 1e3) / 1e9,
                        "hbm_frac": b / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBPS}}
@@ -508,13 +522,9 @@ class E2ELayer:
         per_block = sum(qsakv.cache_bytes(kind, 1, 64, 2, 256))
         self.pool_blocks = wl.E2E_POOL_BYTES // per_block
         e = wl.e2e(self.pool_blocks, device="cuda", seed=seed)
-        ks = vs = 1.0
-        if kind == "e4m3":
-            # per-layer scales max|x| / 448 over everything the layer holds
-            amax_k = torch.cat([e.ctx_k, e.chunk_k, e.step_k]).abs().max().float().item()
-            amax_v = torch.cat([e.ctx_v, e.chunk_v, e.step_v]).abs().max().float().item()
-            ks = float(np.float32(amax_k) / np.float32(448))
-            vs = float(np.float32(amax_v) / np.float32(448))
+        # per-layer scales (E4M3, NVFP4) over everything the layer holds
+        ks, vs = layer_scales(kind, torch.cat([e.ctx_k, e.chunk_k, e.step_k]),
+                              torch.cat([e.ctx_v, e.chunk_v, e.step_v]))
         self.c = qsakv.Cache(kind, self.pool_blocks, 64, 2, 256, k_scale=ks, v_scale=vs,
                              zero=False)
         qsakv.kv_quant_write(self.c, e.ctx_k, e.ctx_v, torch.from_numpy(e.ctx_slots).cuda())
@@ -562,7 +572,7 @@ def bench_e2e(args):
     stream = torch.cuda.current_stream()
     L = args.layers or 2
     arms = {}
-    for kind in ("int8", "bf16", "e4m3"):
+    for kind in ("int8", "bf16", "e4m3", "nvfp4"):
         log("building %d e2e layers (%s)" % (L, kind))
         layers = [E2ELayer(kind, 5 + 100 * i) for i in range(L)]
         for lay in layers:       # the step's inputs are device-resident before timing
@@ -619,14 +629,14 @@ def bench_write(args):
     sm = torch.from_numpy(w.slot_mapping).cuda()
     T = w.slot_mapping.size
     arms = {}
-    for kind in ("int8", "e4m3"):
+    for kind in ("int8", "e4m3", "nvfp4"):
         c = qsakv.Cache(kind, w.num_blocks, w.block_size, 2, 256, k_scale=0.05, v_scale=0.05,
                         zero=False)
         total, _, _ = timed_loop(lambda i: qsakv.kv_quant_write(c, w.k_src, w.v_src, sm,
                                                                 stream=stream),
                                  args.steps, args.warmup, stream)
         ms = total / args.steps
-        per_tok = 2 * 2 * (2 * 256 + (256 + 4 if kind == "int8" else 256))
+        per_tok = 2 * 2 * (2 * 256 + {"int8": 256 + 4, "e4m3": 256, "nvfp4": 128 + 16}[kind])
         arms[kind] = {"ms": ms, "tokens_per_s": T / (ms / 1e3),
                       "GBps": T * per_tok / (ms / 1e3) / 1e9, "bytes_per_token": per_tok}
         del c
@@ -667,6 +677,8 @@ def main():
                              "topk", "copy"])
     ap.add_argument("--layers", type=int, default=0)
     ap.add_argument("--splits", type=int, default=8)
+    ap.add_argument("--kind", default=None, choices=["int8", "e4m3", "bf16", "nvfp4"],
+                    help="cache kind of the decode / e4m3 configs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     args = ap.parse_args()
