@@ -348,9 +348,10 @@ struct RegKeys {
 // position order and the remaining digits over them -- or, when the
 // candidates overflow LDS (heavy ties), the remaining passes re-read the row.
 template <typename R, int KPT, typename O>
-__device__ __forceinline__ void select_row(Smem& s, uint32_t* s_key, int32_t* s_idx,
-                                           const RegKeys<R, KPT>& rk, const R& row, const O& o,
-                                           int k) {
+__device__ __forceinline__ void select_row(Smem& s, uint32_t* s_cand, const RegKeys<R, KPT>& rk,
+                                           const R& row, const O& o, int k) {
+  uint32_t* s_key = s_cand;                              // candidates: keys, then indices
+  int32_t* s_idx = reinterpret_cast<int32_t*>(s_cand + kCand);
   constexpr int kVec = R::kVec;
   constexpr int kGroups = KPT / kVec;
   const auto& key = rk.key;
@@ -359,14 +360,27 @@ __device__ __forceinline__ void select_row(Smem& s, uint32_t* s_key, int32_t* s_
   const int w = (int)uniform(tid / kWave);
   BlockScan bs{s};
   clear_hists(s);
+  for (int i = tid; i < 2 * kCand; i += kThreads) s_cand[i] = 0u;
   __syncthreads();
 
   // ---- first digit, from registers -------------------------------------------
+  // Four histogram copies in the (not yet used) candidate buffer, lane l
+  // counting into copy l mod 4 with its bins XOR-swizzled by the copy index:
+  // lanes of one instruction that hit a hot bin land on different
+  // addresses and banks.  The copies are summed into s.hist[0].
   Sel st{0u, 0u, (uint32_t)k};
+  {
+    const uint32_t cp = (uint32_t)lane & 3u;
+    uint32_t* h4 = s_cand + cp * kBins;
 #pragma unroll
-  for (int j = 0; j < kGroups; ++j)
+    for (int j = 0; j < kGroups; ++j)
 #pragma unroll
-    for (int e = 0; e < kVec; ++e) atomicAdd(&s.hist[0][key[j][e] >> kShift[0]], 1u);
+      for (int e = 0; e < kVec; ++e) atomicAdd(&h4[(key[j][e] >> kShift[0]) ^ cp], 1u);
+  }
+  __syncthreads();
+  for (int b = tid; b < kBins; b += kThreads)
+    s.hist[0][b] = s_cand[b] + s_cand[kBins + (b ^ 1)] + s_cand[2 * kBins + (b ^ 2)] +
+                   s_cand[3 * kBins + (b ^ 3)];
   __syncthreads();
   const uint32_t bin0 = pick_digit(s, s.hist[0], kShift[0], kWidth[0], st);
   // keys with a top digit above d0 are all listed; d0's bin holds the rest
@@ -476,8 +490,7 @@ template <int SRC, int KPT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
 void topk_cand_kernel(TopkParams p) {
   __shared__ Smem s;
-  __shared__ uint32_t s_key[kCand];
-  __shared__ int32_t s_idx[kCand];
+  __shared__ uint32_t s_cand[2 * kCand];
   const int r = blockIdx.x, k = p.topk;
   int32_t* out = p.out + (int64_t)r * k;
   const int n = min(max(p.row_len[r], 0), p.row_stride);
@@ -488,7 +501,7 @@ void topk_cand_kernel(TopkParams p) {
   const ScoreRow<SRC> row{row_ptr<SRC>(p, r), n, 0};
   RegKeys<ScoreRow<SRC>, KPT> rk;
   rk.load(row);
-  select_row(s, s_key, s_idx, rk, row, ListOut{out}, k);
+  select_row(s, s_cand, rk, row, ListOut{out}, k);
 }
 
 // Long rows, stage 1: segment s (positions [s L, (s + 1) L)) of row r
@@ -501,8 +514,7 @@ template <int SRC, int KPT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
 void topk_seg_kernel(TopkParams p) {
   __shared__ Smem s;
-  __shared__ uint32_t s_key[kCand];
-  __shared__ int32_t s_idx[kCand];
+  __shared__ uint32_t s_cand[2 * kCand];
   const int seg = blockIdx.x, r = blockIdx.y, k = p.topk, L = p.seg_len;
   const int n = min(max(p.row_len[r], 0), p.row_stride);
   const int ns = min(max(n - seg * L, 0), L);
@@ -523,7 +535,7 @@ void topk_seg_kernel(TopkParams p) {
       }
     return;
   }
-  select_row(s, s_key, s_idx, rk, row, o, k);
+  select_row(s, s_cand, rk, row, o, k);
 }
 
 // Long rows, stage 2: the segments' lists of row r, concatenated (every
@@ -533,8 +545,7 @@ template <int KPT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
 void topk_merge_kernel(TopkParams p) {
   __shared__ Smem s;
-  __shared__ uint32_t s_key[kCand];
-  __shared__ int32_t s_idx[kCand];
+  __shared__ uint32_t s_cand[2 * kCand];
   const int r = blockIdx.x, k = p.topk, L = p.seg_len;
   int32_t* out = p.out + (int64_t)r * k;
   const int n = min(max(p.row_len[r], 0), p.row_stride);
@@ -548,7 +559,7 @@ void topk_merge_kernel(TopkParams p) {
   }
   RegKeys<KeyRow, KPT> rk;
   rk.load(row);
-  select_row(s, s_key, s_idx, rk, row, ListOut{out}, k);
+  select_row(s, s_cand, rk, row, ListOut{out}, k);
 }
 
 }  // namespace
