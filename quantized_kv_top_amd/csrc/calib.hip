@@ -31,6 +31,7 @@ constexpr int kMaxPass1 = 256;     // streaming workgroups (one per CU)
 
 constexpr int kRedThreads = 256;
 constexpr int kRedBlocks = kBins / kRedThreads;   // 128
+constexpr int kRedSplit = 4;      // threads per key in the reduction
 
 // Workspace, in uint64 words: [hist1 32768][hist2 2 x 65536][sel 8]
 // [per-workgroup counters 256 x 8][per-reduction-block counters 128 x 8],
@@ -216,48 +217,59 @@ __device__ __forceinline__ void block_reduce6(unsigned long long (&v)[N],
   }
 }
 
-// One thread per key: hist1[key] = the workgroups' slots summed (16 slots in
-// flight per thread), NaN keys of 16-bit sources set aside; each block then
-// leaves its counts (16-bit sources: classified per key, exact since the key
-// is the value) and the sum of its bins for the selection.
-__global__ __launch_bounds__(kRedThreads) void calib_reduce_kernel(CalibParams p) {
-  __shared__ unsigned long long s_red[kRedThreads / kWave][8];
+// kRedSplit threads per key, each summing every kRedSplit-th workgroup
+// slot (16 slots in flight per thread), then the parts added in LDS:
+// hist1[key] = the workgroups' slots summed, NaN keys of 16-bit sources set
+// aside; each block then leaves its counts (16-bit sources: classified per
+// key, exact since the key is the value) and the sum of its bins for the
+// selection.
+__global__ __launch_bounds__(kRedThreads * kRedSplit) void calib_reduce_kernel(CalibParams p) {
+  __shared__ unsigned long long s_red[kRedThreads * kRedSplit / kWave][8];
+  __shared__ unsigned long long s_part[kRedSplit][kRedThreads];
   const Ws w = ws_of(p);
-  const uint32_t key = blockIdx.x * kRedThreads + threadIdx.x;
+  const int t = threadIdx.x % kRedThreads, part = threadIdx.x / kRedThreads;
+  const uint32_t key = blockIdx.x * kRedThreads + t;
   constexpr int kIn = 16;
   unsigned long long h = 0;
-  for (int g0 = 0; g0 < p.grid1; g0 += kIn) {
+  for (int g0 = part; g0 < p.grid1; g0 += kIn * kRedSplit) {
     uint32_t v[kIn];
 #pragma unroll
-    for (int u = 0; u < kIn; ++u)
-      v[u] = g0 + u < p.grid1 ? w.wg_hist[(int64_t)(g0 + u) * kBins + key] : 0u;
+    for (int u = 0; u < kIn; ++u) {
+      const int g = g0 + u * kRedSplit;
+      v[u] = g < p.grid1 ? w.wg_hist[(int64_t)g * kBins + key] : 0u;
+    }
 #pragma unroll
     for (int u = 0; u < kIn; ++u) h += v[u];
   }
+  s_part[part][t] = h;
+  __syncthreads();
   unsigned long long c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (p.src_dtype != kDtFP32) {
-    const uint32_t ab = key_bits(p.src_dtype, key);
-    if (ab > 0x7F800000u) {
-      c[kCntNan] = h;
-      h = 0;
-    } else {
-      c[kCntNonzero] = ab != 0u ? h : 0ull;
-      c[kCntSat] = ab >= p.t_sat ? h : 0ull;
-      c[kCntBelow] = (ab != 0u && ab < p.t_sub) ? h : 0ull;
-      c[kCntSub] = (ab >= p.t_sub && ab < p.t_norm) ? h : 0ull;
-      c[kCntAmax] = h ? ab : 0u;
+  if (part == 0) {
+#pragma unroll
+    for (int q = 1; q < kRedSplit; ++q) h += s_part[q][t];
+    if (p.src_dtype != kDtFP32) {
+      const uint32_t ab = key_bits(p.src_dtype, key);
+      if (ab > 0x7F800000u) {
+        c[kCntNan] = h;
+        h = 0;
+      } else {
+        c[kCntNonzero] = ab != 0u ? h : 0ull;
+        c[kCntSat] = ab >= p.t_sat ? h : 0ull;
+        c[kCntBelow] = (ab != 0u && ab < p.t_sub) ? h : 0ull;
+        c[kCntSub] = (ab >= p.t_sub && ab < p.t_norm) ? h : 0ull;
+        c[kCntAmax] = h ? ab : 0u;
+      }
+    } else if (blockIdx.x == 0 && t < 6) {
+      // fp32: the streaming pass classified the elements; sum its counters
+      // (one field per thread, then spread through the block reduction)
+      for (int g = 0; g < p.grid1; ++g) {
+        const unsigned long long x = w.wg_cnt[g * 8 + t];
+        c[t] = t == kCntAmax ? (x > c[t] ? x : c[t]) : c[t] + x;
+      }
     }
-  } else if (blockIdx.x == 0 && threadIdx.x < 6) {
-    // fp32: the streaming pass classified the elements; sum its counters
-    // (one field per thread, then spread through the block reduction)
-    for (int g = 0; g < p.grid1; ++g) {
-      const unsigned long long x = w.wg_cnt[g * 8 + threadIdx.x];
-      c[threadIdx.x] = threadIdx.x == kCntAmax ? (x > c[threadIdx.x] ? x : c[threadIdx.x])
-                                               : c[threadIdx.x] + x;
-    }
+    w.hist1[key] = h;
+    c[kCntBins] = h;
   }
-  w.hist1[key] = h;
-  c[kCntBins] = h;
   block_reduce6<8>(c, s_red);
   if (threadIdx.x < 8) w.blk[blockIdx.x * 8 + threadIdx.x] = c[threadIdx.x];
 }
@@ -328,25 +340,30 @@ __global__ __launch_bounds__(kRedThreads) void calib_select_kernel(CalibParams p
   const unsigned long long bexcl = block_exscan(bsum, s_tmp, tot);
   const unsigned long long k[2] = {(999ull * m + 999ull) / 1000ull,      // ceil(999 m / 1000)
                                    (9999ull * m + 9999ull) / 10000ull};  // ceil(9999 m / 10000)
-  for (int q = 0; q < 2; ++q) {
-    __shared__ unsigned long long s_blk[2];
+  // both ranks' blocks first, so that their bin loads go out together
+  __shared__ unsigned long long s_blk[2][2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
     if (t < kRedBlocks && m > 0 && k[q] > bexcl && k[q] <= bexcl + bsum) {
-      s_blk[0] = t;
-      s_blk[1] = bexcl;
+      s_blk[q][0] = t;
+      s_blk[q][1] = bexcl;
     }
-    __syncthreads();
-    if (m > 0) {
-      const unsigned long long blk = s_blk[0];
-      const unsigned long long h = w.hist1[blk * kRedThreads + t];
+  __syncthreads();
+  if (m > 0) {                                        // uniform
+    unsigned long long h[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) h[q] = w.hist1[s_blk[q][0] * kRedThreads + t];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
       unsigned long long all;
-      const unsigned long long ex = s_blk[1] + block_exscan(h, s_tmp, all);
-      if (k[q] > ex && k[q] <= ex + h) {
-        s_pick[2 * q] = blk * kRedThreads + t;
+      const unsigned long long ex = s_blk[q][1] + block_exscan(h[q], s_tmp, all);
+      if (k[q] > ex && k[q] <= ex + h[q]) {
+        s_pick[2 * q] = s_blk[q][0] * kRedThreads + t;
         s_pick[2 * q + 1] = k[q] - ex;
       }
     }
-    __syncthreads();
   }
+  __syncthreads();
   if (t == 0) {
     const bool k16 = p.src_dtype != kDtFP32;
     qkv_calib_result r;
@@ -453,7 +470,7 @@ hipError_t launch_calib(const CalibParams& p, hipStream_t s) {
     default: e = launch_src<kDtFP16>(q, q.grid1, s); break;
   }
   if (e != hipSuccess) return e;
-  calib_reduce_kernel<<<kRedBlocks, dim3(kRedThreads), 0, s>>>(q);
+  calib_reduce_kernel<<<kRedBlocks, dim3(kRedThreads * kRedSplit), 0, s>>>(q);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   calib_select_kernel<<<1, dim3(kRedThreads), 0, s>>>(q);
