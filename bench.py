@@ -296,7 +296,7 @@ def bench_decode(args):
     layers = []
     for i in range(L):
         w = wl.decode(device="cuda", seed=200 + i)
-        layers.append(DecodeLayer(w, kind, *layer_scales(kind, w.k_src, w.v_src)))
+        layers.append(DecodeLayer(w, kind, *layer_scales(kind, w.k_src, w.v_src), args.splits))
     torch.cuda.synchronize()
     total, per = graph_loop(layers, args.steps, args.warmup, 1)
     calls = args.steps * L
@@ -309,8 +309,8 @@ def bench_decode(args):
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": kind,
             "data": "synthetic",
             "config": {"workload": "decode: 8 seqs x 128K ctx, 5 rows each (40), top-k 2048 "
-                                   "(70%% recent window), split-K 8 + merge, %s cache; "
-                                   "%d layers rotated, graph-captured" % (kind, L),
+                                   "(70%% recent window), split-K %d + merge, %s cache; "
+                                   "%d layers rotated, graph-captured" % (args.splits, kind, L),
                        "gathered_kv_bytes_per_call": b,
                        "gathered_kv_GBps": b / (ms_call / 1e3) / 1e9,
                        "hbm_frac": b / (ms_call / 1e3) / 1e9 / HBM_PEAK_GBPS}}

@@ -548,7 +548,21 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
                                                             : -1;
     }
   };
-  if (npos > 0) chunk_finish(0);    // block-table loads in flight during the query setup
+  if (npos > 0) chunk_finish(0);
+
+  // ---- the wave's first two tiles go out before the query setup ------------
+  // tiles w, w + NW, w + 2 NW, ... of a chunk, kDepth of them in registers:
+  // kDepth - 1 in flight while one is computed
+  __syncthreads();                   // the first chunk's slots are published
+  auto ts = [&](int k) { return s_slot + (w + NW * k) * TT; };
+  auto wave_tiles = [&](int c0) {
+    const int ntiles = (min(kChunk, npos - c0) + TT - 1) / TT;
+    return ntiles > w ? (ntiles - w + NW - 1) / NW : 0;
+  };
+  int my_n = npos > 0 ? wave_tiles(0) : 0;
+  TileRaw<KIND, D, TT> ta, tb;
+  if (my_n > 0) issue_tile<KIND, D, TT>(ta, p, g, ts(0));
+  if (my_n > 1) issue_tile<KIND, D, TT>(tb, p, g, ts(1));
 
   // ---- Q operand (B of QK^T), the logit factor and the int8 bias term ----
   QOp<KIND> qop[G::kQK];
@@ -605,11 +619,12 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
   using QS = std::conditional_t<G::kQLds, QLds<KIND>, QRegs<KIND, G::kQK>>;
   QS qs;
   if constexpr (G::kQLds) {
-    if (w == 0) {          // published by the barrier ahead of the first tile
+    if (w == 0) {          // published by the barrier below
 #pragma unroll
       for (int i = 0; i < G::kQK; ++i) s_q[i * kWave + lane] = qop[i];
     }
     qs.p = s_q + lane;
+    __syncthreads();
   } else {
 #pragma unroll
     for (int i = 0; i < G::kQK; ++i) qs.v[i] = qop[i];
@@ -626,16 +641,11 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
       __syncthreads();               // the previous chunk's slots are consumed
       chunk_start(c0);
       chunk_finish(c0);
+      __syncthreads();
+      my_n = wave_tiles(c0);
+      if (my_n > 0) issue_tile<KIND, D, TT>(ta, p, g, ts(0));
+      if (my_n > 1) issue_tile<KIND, D, TT>(tb, p, g, ts(1));
     }
-    __syncthreads();
-    const int ntiles = (min(kChunk, npos - c0) + TT - 1) / TT;
-    const int my_n = ntiles > w ? (ntiles - w + NW - 1) / NW : 0;
-    // tiles w, w + NW, w + 2 NW, ... of the chunk, kDepth of them in
-    // registers: kDepth - 1 in flight while one is computed
-    auto ts = [&](int k) { return s_slot + (w + NW * k) * TT; };
-    TileRaw<KIND, D, TT> ta, tb;
-    if (my_n > 0) issue_tile<KIND, D, TT>(ta, p, g, ts(0));
-    if (my_n > 1) issue_tile<KIND, D, TT>(tb, p, g, ts(1));
     for (int k = 0; k < my_n; k += 2) {
       compute_tile<KIND, D, TT, QS>(ta, qs, kfac, kbias, st, o);
       if (k + 2 < my_n) issue_tile<KIND, D, TT>(ta, p, g, ts(k + 2));
