@@ -472,7 +472,11 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
   constexpr int kChunk = kPer * kThreads;   // list positions resolved per LDS batch
   __shared__ __align__(16) int s_slot[kChunk];
   __shared__ float s_m[NW][16], s_l[NW][16];
-  __shared__ f32x4 s_obuf[NW > 1 ? NW / 2 : 1][G::kPV * kWave];
+  // cross-wave merge: two waves pair up (one buffer); four or eight waves
+  // each park their accumulator (one buffer per wave)
+  constexpr int kObufs = NW >= 4 ? NW : 1;
+  __shared__ f32x4 s_obuf[kObufs][G::kPV * kWave];
+  __shared__ float s_sig[NW];
   __shared__ QOp<KIND> s_q[G::kQLds ? G::kQK * kWave : 1];
 
   const int lane = lane_id(), ln16 = lane & 15, grp = lane >> 4;
@@ -657,10 +661,13 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
   }
 
   // ---- merge the waves' partial results -----------------------------------
-  // Each wave brings its accumulator to the common max M (and, for int8, to
-  // scale 1 from its reference V scale); the waves are then summed pairwise
-  // in LDS, upper half onto lower half (a fixed order: bitwise
-  // reproducible), leaving the total in wave 0.
+  // Each wave's accumulator is weighted by exp2(m_w - M) (and, for int8, its
+  // reference V scale) toward the common max M.  Two waves: the upper one
+  // parks its weighted accumulator in LDS and the lower one adds it.  Four or
+  // eight waves: every wave parks its raw accumulator, then wave w sums
+  // slices j = w, w + NW, ... over the waves in wave order and leaves them in
+  // wave 0's buffer -- two barriers in all, a fixed order (bitwise
+  // reproducible); the total ends in wave 0.
   const float l_h = group4_sum(st.l);
   if constexpr (G::kInt) {
     const float corr = kI8Bias * group4_sum(st.cw);
@@ -671,35 +678,55 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
     s_m[w][ln16] = st.m;
     s_l[w][ln16] = l_h;
   }
+  if constexpr (NW >= 4) {
+    if (lane == 0) s_sig[w] = G::kInt ? st.sig : 1.f;
+#pragma unroll
+    for (int j = 0; j < G::kPV; ++j) s_obuf[w][j * kWave + lane] = o[j];
+  }
   __syncthreads();
   float M = kNegInf;
 #pragma unroll
   for (int i = 0; i < NW; ++i) M = fmaxf(M, s_m[i][ln16]);
-  float L = 0.f, myf = 0.f;
+  float L = 0.f, f[NW];
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
     const float mi = s_m[i][ln16];
-    const float f = mi == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mi - M);
-    L += f * s_l[i][ln16];
-    if (i == w) myf = f;
+    f[i] = mi == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mi - M);
+    L += f[i] * s_l[i][ln16];
   }
-  if constexpr (G::kInt) myf *= st.sig;
+  if constexpr (NW >= 4) {
 #pragma unroll
-  for (int j = 0; j < G::kPV; ++j) o[j] *= myf;
+    for (int i = 0; i < NW; ++i) f[i] *= s_sig[i];
+    for (int j = w; j < G::kPV; j += NW) {
+      f32x4 acc = s_obuf[0][j * kWave + lane] * f[0];
 #pragma unroll
-  for (int half = NW / 2; half >= 1; half >>= 1) {
-    if (w >= half && w < 2 * half) {
-      f32x4* buf = s_obuf[w - half];
-#pragma unroll
-      for (int j = 0; j < G::kPV; ++j) buf[j * kWave + lane] = o[j];
+      for (int i = 1; i < NW; ++i) acc += s_obuf[i][j * kWave + lane] * f[i];
+      s_obuf[0][j * kWave + lane] = acc;
     }
     __syncthreads();
-    if (w < half) {
-      const f32x4* buf = s_obuf[w];
+    if (w == 0) {
 #pragma unroll
-      for (int j = 0; j < G::kPV; ++j) o[j] += buf[j * kWave + lane];
+      for (int j = 0; j < G::kPV; ++j) o[j] = s_obuf[0][j * kWave + lane];
     }
-    if (half > 1) __syncthreads();    // the next step overwrites these buffers
+  } else if constexpr (NW == 2) {
+    float myf = f[w];
+    if constexpr (G::kInt) myf *= st.sig;
+#pragma unroll
+    for (int j = 0; j < G::kPV; ++j) o[j] *= myf;
+    if (w == 1) {
+#pragma unroll
+      for (int j = 0; j < G::kPV; ++j) s_obuf[0][j * kWave + lane] = o[j];
+    }
+    __syncthreads();
+    if (w == 0) {
+#pragma unroll
+      for (int j = 0; j < G::kPV; ++j) o[j] += s_obuf[0][j * kWave + lane];
+    }
+  } else {
+    float myf = f[0];
+    if constexpr (G::kInt) myf *= st.sig;
+#pragma unroll
+    for (int j = 0; j < G::kPV; ++j) o[j] *= myf;
   }
   if (w != 0 || !head_ok) return;
 
