@@ -179,6 +179,53 @@ def cpu_baseline_prefill(seed, budget_s, rows_cap):
             "one_thread_gathered_GBps": done1 / el1 * per_row / 1e9}
 
 
+def cpu_baseline_rows(make_workloads, kind, budget_s, what):
+    """The oracle, as it stands, on whole small launches: each workload's
+    listed tokens (only those) quantized into an oracle cache, then its rows'
+    attention, timed with all BLAS threads (the reported value) and again on
+    one thread."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from oracle import attention as oatt
+    from oracle import cache as ocache
+
+    jobs = []
+    per_row = 0
+    for w in make_workloads():
+        ks, vs = layer_scales(kind, w.k_src, w.v_src)
+        oc = ocache.OracleCache(kind, w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim,
+                                k_scale=ks, v_scale=vs)
+        ctx = w.slot_mapping.size // (int(w.row_seq.max()) + 1)
+        tok = np.unique((w.row_seq.astype(np.int64)[:, None] * ctx + w.topk_idx).ravel())
+        oc.write(wl.to_numpy_src(w.k_src)[tok], wl.to_numpy_src(w.v_src)[tok], w.src_dtype,
+                 w.slot_mapping[tok])
+        jobs.append((oc, wl.to_numpy_src(w.q), w))
+        per_row = gathered_bytes_per_row(kind, w.topk, w.num_kv_heads, w.head_dim)
+    nrows = sum(j[2].num_rows for j in jobs)
+
+    def rate(budget):
+        # the rows in order, cycled until the budget is spent
+        done, t0 = 0, time.perf_counter()
+        while True:
+            for oc, qn, w in jobs:
+                for r in range(w.num_rows):
+                    if time.perf_counter() - t0 >= budget:
+                        return done, time.perf_counter() - t0
+                    oatt.sparse_attention(oc, qn, w.q_dtype, w.row_seq, w.block_table,
+                                          w.topk_idx, w.sm_scale, rows=[r])
+                    done += 1
+
+    done, el = rate(budget_s)
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    with threadpool_limits(limits=1):
+        done1, el1 = rate(budget_s / 3)
+    return {"value": done / el, "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": "%d rows (%s, %d rows cycled; %s cache, fp64 numpy) in %.1f s with %d "
+                      "BLAS threads" % (done, what, nrows, kind, el, threads),
+            "gathered_GBps": done / el * per_row / 1e9,
+            "one_thread_rows_per_s": done1 / el1,
+            "one_thread_gathered_GBps": done1 / el1 * per_row / 1e9}
+
+
 def bench_prefill(args):
     stream = torch.cuda.current_stream()
     rows, topk = 2048, 1024
@@ -304,6 +351,12 @@ def bench_decode(args):
     w = layers[0].w
     rows = w.num_rows
     b = rows * gathered_bytes_per_row(kind, w.topk, 2, 256)
+    cpu = None
+    if not args.no_cpu_baseline:
+        del layers
+        torch.cuda.empty_cache()
+        cpu = cpu_baseline_rows(lambda: [wl.decode(device="cpu", seed=200)], kind,
+                                args.cpu_budget, "all 40 decode rows of one layer, top-k 2048")
     return {"metric": METRIC, "value": rows / (ms_call / 1e3), "unit": "rows/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_call,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": kind,
@@ -313,7 +366,8 @@ def bench_decode(args):
                                    "%d layers rotated, graph-captured" % (args.splits, kind, L),
                        "gathered_kv_bytes_per_call": b,
                        "gathered_kv_GBps": b / (ms_call / 1e3) / 1e9,
-                       "hbm_frac": b / (ms_call / 1e3) / 1e9 / HBM_PEAK_GBPS}}
+                       "hbm_frac": b / (ms_call / 1e3) / 1e9 / HBM_PEAK_GBPS},
+            "cpu_baseline": cpu}
 
 
 def bench_e4m3(args):
@@ -331,8 +385,15 @@ def bench_e4m3(args):
     total, per = graph_loop(layers, args.steps, args.warmup, 1)
     ms_step = total / args.steps / sets          # one 12-layer step
     w = layers[0].w
-    b = L * w.num_rows * gathered_bytes_per_row(kind, w.topk, 4, 128)
-    return {"metric": METRIC, "value": L * w.num_rows / (ms_step / 1e3),
+    rows = w.num_rows
+    b = L * rows * gathered_bytes_per_row(kind, w.topk, 4, 128)
+    cpu = None
+    if not args.no_cpu_baseline:
+        del layers, w
+        torch.cuda.empty_cache()
+        cpu = cpu_baseline_rows(lambda: [wl.e4m3_layer(i, device="cpu", seed=4) for i in range(3)],
+                                kind, args.cpu_budget, "the 4 rows of layers 0-2 of 12")
+    return {"metric": METRIC, "value": L * rows / (ms_step / 1e3),
             "unit": "layer-rows/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": kind, "data": "synthetic",
@@ -341,7 +402,8 @@ def bench_e4m3(args):
                                    "graph-captured" % (kind, splits, sets),
                        "gathered_kv_bytes_per_step": b,
                        "gathered_kv_GBps": b / (ms_step / 1e3) / 1e9,
-                       "hbm_frac": b / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBPS}}
+                       "hbm_frac": b / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBPS},
+            "cpu_baseline": cpu}
 
 
 class MixedLayer:
