@@ -96,7 +96,7 @@ def test_mixed_catch_up_and_decode_rows_one_launch():
         check(o, l, ro, rl, "mixed P%d" % P)
 
 
-@pytest.mark.parametrize("kind", ["int8", "e4m3", "bf16"])
+@pytest.mark.parametrize("kind", ["int8", "e4m3", "bf16", "nvfp4"])
 def test_e2e_layer_step(kind):
     """Existing context + an 8192-token chunk written (quantize-on-write) and
     attended with top-k 1024, then 8 decode steps of one new token each with
@@ -107,12 +107,13 @@ def test_e2e_layer_step(kind):
     e = wl.e2e(pool_blocks, device="cuda")
     say("e2e", kind, "pool blocks", pool_blocks)
     ks = vs = 1.0
-    if kind == "e4m3":
+    if kind in ("e4m3", "nvfp4"):
         allk = torch.cat([e.ctx_k, e.chunk_k, e.step_k]).abs().max().float().item()
         allv = torch.cat([e.ctx_v, e.chunk_v, e.step_v]).abs().max().float().item()
         from oracle import formats as ofmt
-        ks = float(ofmt.e4m3_calibrate_scale(np.array([allk], np.float32)))
-        vs = float(ofmt.e4m3_calibrate_scale(np.array([allv], np.float32)))
+        cal = ofmt.e4m3_calibrate_scale if kind == "e4m3" else ofmt.nvfp4_calibrate_scale
+        ks = float(cal(np.array([allk], np.float32)))
+        vs = float(cal(np.array([allv], np.float32)))
     c = qsakv.Cache(kind, pool_blocks, 64, 2, 256, k_scale=ks, v_scale=vs, zero=False)
     qsakv.kv_quant_write(c, e.ctx_k, e.ctx_v, dev(e.ctx_slots, torch.int64))
     qsakv.kv_quant_write(c, e.chunk_k, e.chunk_v, dev(e.chunk_slots, torch.int64))
@@ -153,7 +154,11 @@ def test_e2e_layer_step(kind):
     np.testing.assert_array_equal(got[0], compact.oc.k)
     np.testing.assert_array_equal(got[1], compact.oc.v)
     if got[2] is not None:
-        np.testing.assert_array_equal(got[2].view(np.uint32), compact.oc.kv_scale.view(np.uint32))
+        want = compact.oc.kv_scale
+        if want.dtype == np.float32:
+            np.testing.assert_array_equal(got[2].view(np.uint32), want.view(np.uint32))
+        else:                                   # NVFP4 block-scale bytes
+            np.testing.assert_array_equal(got[2], want.reshape(got[2].shape))
     del c
     torch.cuda.empty_cache()
 
@@ -173,8 +178,9 @@ class _CompactOracle:
         self.slots = self.slots[order]
         toks = toks[order]
         n = toks.size
-        self.oc = ocache.OracleCache(kind, n, 1, 2, 256, ks if kind == "e4m3" else None,
-                                     vs if kind == "e4m3" else None)
+        scaled = kind in ("e4m3", "nvfp4")
+        self.oc = ocache.OracleCache(kind, n, 1, 2, 256, ks if scaled else None,
+                                     vs if scaled else None)
         ti = torch.as_tensor(toks).to(w.k_src.device)
         self.oc.write(wl.to_numpy_src(w.k_src[ti]), wl.to_numpy_src(w.v_src[ti]), "bf16",
                       np.arange(n))
