@@ -374,39 +374,35 @@ __device__ __forceinline__ void compute_tile(const TileRaw<KIND, D, TT>& t, cons
       }
     }
   } else if constexpr (G::kFp4) {
-    // token e's word c: 8 codes = the lane's d-values 8 c .. 8 c + 7, times
-    // the token's block scale (exact in fp16); the A operand of d-value dd
-    // gathers the four tokens' halves
+    // token e's word c: 8 codes = the lane's d-values 8 c .. 8 c + 7.  The
+    // words of token pairs (0, 1) and (2, 3) are nibble-interleaved: byte j
+    // of x01 holds token 0's and token 1's codes of one d-value, so its FP4
+    // conversion is the (token 0, token 1) half of the A operand; times the
+    // pair's block scales, exact in fp16.
     f16x4 bw;
 #pragma unroll
     for (int e = 0; e < 4; ++e) bw[e] = (_Float16)w[e];
-    f16x2 sc2[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t scb = (t.vsc >> (8 * e)) & 0xFFu;
-      sc2[e] = bitcast<f16x2>(e4m3pair_to_f16x2<false>(scb | (scb << 8)));
-    }
+    const f16x2 sc01 = bitcast<f16x2>(e4m3pair_to_f16x2<false>(t.vsc));
+    const f16x2 sc23 = bitcast<f16x2>(e4m3pair_to_f16x2<true>(t.vsc));
 #pragma unroll
     for (int c = 0; c < G::kVWords; ++c) {
+      const uint32_t w0 = t.v[0][c], w1 = t.v[1][c], w2 = t.v[2][c], w3 = t.v[3][c];
+      const uint32_t x01[2] = {(w0 & 0x0F0F0F0Fu) | ((w1 << 4) & 0xF0F0F0F0u),    // low nibbles
+                               ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u)};  // high nibbles
+      const uint32_t x23[2] = {(w2 & 0x0F0F0F0Fu) | ((w3 << 4) & 0xF0F0F0F0u),
+                               ((w2 >> 4) & 0x0F0F0F0Fu) | (w3 & 0xF0F0F0F0u)};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        uint32_t r[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          uint32_t pr;
-          const uint32_t wv = t.v[e][c];
-          if (j == 0) pr = e2m1pair_to_f16x2<0>(wv);
-          else if (j == 1) pr = e2m1pair_to_f16x2<1>(wv);
-          else if (j == 2) pr = e2m1pair_to_f16x2<2>(wv);
-          else pr = e2m1pair_to_f16x2<3>(wv);
-          r[e] = bitcast<uint32_t>(bitcast<f16x2>(pr) * sc2[e]);
-        }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const uint32_t sel = h ? 0x07060302u : 0x05040100u;
+          uint32_t p01, p23;
+          if (j == 0) { p01 = e2m1pair_to_f16x2<0>(x01[h]); p23 = e2m1pair_to_f16x2<0>(x23[h]); }
+          else if (j == 1) { p01 = e2m1pair_to_f16x2<1>(x01[h]); p23 = e2m1pair_to_f16x2<1>(x23[h]); }
+          else if (j == 2) { p01 = e2m1pair_to_f16x2<2>(x01[h]); p23 = e2m1pair_to_f16x2<2>(x23[h]); }
+          else { p01 = e2m1pair_to_f16x2<3>(x01[h]); p23 = e2m1pair_to_f16x2<3>(x23[h]); }
           u32x2 a;
-          a[0] = perm(r[1], r[0], sel);
-          a[1] = perm(r[3], r[2], sel);
+          a[0] = bitcast<uint32_t>(bitcast<f16x2>(p01) * sc01);
+          a[1] = bitcast<uint32_t>(bitcast<f16x2>(p23) * sc23);
           o[8 * c + 2 * j + h] = __builtin_amdgcn_mfma_f32_16x16x16f16(bitcast<f16x4>(a), bw,
                                                                       o[8 * c + 2 * j + h], 0, 0, 0);
         }
