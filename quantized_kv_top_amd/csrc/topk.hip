@@ -14,7 +14,8 @@
 // whose integer order is the ranking (-0 folded onto +0, sign-magnitude
 // flip, NaN to 0).  One workgroup of 1024 threads per row, two per CU:
 //   * the row is read once into registers and turned into keys;
-//   * an LDS histogram of the top 11 key bits gives the digit d0 of the k-th
+//   * an LDS histogram of the top 11 key bits (counted into four copies with
+//     bins XOR-swizzled by copy, then summed) gives the digit d0 of the k-th
 //     largest key (the bins are summed in 16 slices, one barrier, then every
 //     wave locates the digit by itself);
 //   * the keys whose top digit is at least d0 -- the sure ones above d0's bin
