@@ -104,6 +104,81 @@ __device__ __forceinline__ uint32_t e2m1_encode(float y) {
   return ((__float_as_uint(y) >> 28) & 8u) | c;
 }
 
+// Quantize this lane's kEPL elements of one K or V row (lanes part = 0 ..
+// kLPR-1 of the row together) and store the codes at cache row `row` of
+// `base`.  Returns the bits of what the caller stores beside them: the
+// int8 scale s (side layout), or this lane's NVFP4 block-scale code; the
+// inline int8 layout stores its scale itself.
+template <int KIND, int D>
+__device__ __forceinline__ uint32_t quantize_row(const WriteParams& p, uint8_t* base, int64_t row,
+                                              int part, int which, const float (&x)[kEPL]) {
+  constexpr int kLPR = D / kEPL;
+  if constexpr (KIND == kInt8 || KIND == kInt8Inline) {
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < kEPL; ++i) a = fmaxf(a, fabsf(x[i]));
+    a = row_max<kLPR>(a);
+    const float s = a / 127.0f;
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < kEPL; ++i) {
+      float q = 0.f;
+      if (s != 0.f) q = fminf(fmaxf(rintf(x[i] / s), -127.f), 127.f);
+      w[i >> 2] |= ((uint32_t)(int32_t)q & 0xFFu) << (8 * (i & 3));
+    }
+    if constexpr (KIND == kInt8) {
+      *reinterpret_cast<u32x4*>(base + row * D + part * kEPL) = u32x4{w[0], w[1], w[2], w[3]};
+    } else {  // 4-byte-aligned rows of D + 4 bytes
+      uint32_t* dst = reinterpret_cast<uint32_t*>(base + row * (D + 4) + part * kEPL);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i] = w[i];
+      if (part == 0) *reinterpret_cast<float*>(base + row * (D + 4) + D) = s;
+    }
+    return __float_as_uint(s);
+  } else if constexpr (KIND == kE4M3) {
+    const float scale = which ? p.v_scale : p.k_scale;
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < kEPL; ++i) w[i >> 2] |= e4m3_encode(x[i] / scale) << (8 * (i & 3));
+    *reinterpret_cast<u32x4*>(base + row * D + part * kEPL) = u32x4{w[0], w[1], w[2], w[3]};
+    return 0u;
+  } else if constexpr (KIND == kNvfp4) {
+    const float g = which ? p.v_scale : p.k_scale;
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < kEPL; ++i) {   // NaN ignored: a comparison with NaN is false
+      const float v = fabsf(x[i]);     // (a NaN-quieting max could pass a NaN on)
+      a = v > a ? v : a;
+    }
+    const float sb = a / 6.0f;
+    const uint32_t sc = e4m3_encode(sb / g);
+    const float eff = e4m3_value(sc) * g;
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < kEPL; ++i)
+      w[i >> 3] |= (eff > 0.f ? e2m1_encode(x[i] / eff) : 0u) << (4 * (i & 7));
+    *reinterpret_cast<u32x2*>(base + row * (D / 2) + part * 8) = u32x2{w[0], w[1]};
+    return sc;
+  } else {  // kBF16: round to nearest even (identity for bf16 sources)
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      bf16x2 b;
+      b[0] = (__bf16)x[2 * i];
+      b[1] = (__bf16)x[2 * i + 1];
+      w[i] = bitcast<uint32_t>(b);
+    }
+    u32x4* dst = reinterpret_cast<u32x4*>(base + row * (2 * D) + part * (2 * kEPL));
+    dst[0] = u32x4{w[0], w[1], w[2], w[3]};
+    dst[1] = u32x4{w[4], w[5], w[6], w[7]};
+    return 0u;
+  }
+}
+
+// One wave takes kRPW source rows (token, KV head), K and V both: the two
+// rows' sources are loaded together, and the row's K and V scales leave as
+// one store (int8: the fp32 pair; NVFP4: each lane's two block-scale codes,
+// 16-byte K and V runs side by side).
 template <int KIND, int D, int SRC>
 __global__ __launch_bounds__(kWavesPerBlock * kWave) void kv_write_kernel(WriteParams p) {
   constexpr int kLPR = D / kEPL;         // lanes per row
@@ -111,80 +186,29 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void kv_write_kernel(WriteP
   const int lane = lane_id();
   const int sub = lane / kLPR, part = lane % kLPR;
   const int hkv = p.num_kv_heads;
-  const int64_t nrow = p.num_tokens * hkv;                  // rows per stream
-  const int64_t gps = (nrow + kRPW - 1) / kRPW;             // wave groups per stream
+  const int64_t nrow = p.num_tokens * hkv;                  // source rows
+  const int64_t groups = (nrow + kRPW - 1) / kRPW;          // wave groups
   const int64_t stride = (int64_t)gridDim.x * kWavesPerBlock;
-  for (int64_t gi = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6); gi < 2 * gps;
+  for (int64_t gi = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6); gi < groups;
        gi += stride) {
-    const int which = gi >= gps;                            // 0 = K, 1 = V
-    const int64_t r = (gi - which * gps) * kRPW + sub;
+    const int64_t r = gi * kRPW + sub;
     if (r >= nrow) continue;                                // whole rows drop out together
     const int64_t t = r / hkv;
     const int h = (int)(r - t * hkv);
     const int64_t slot = p.slot_mapping[t];
-    float x[kEPL];
-    load_src16<SRC>(which ? p.v_src : p.k_src, r * D + part * kEPL, x);
+    float xk[kEPL], xv[kEPL];
+    load_src16<SRC>(p.k_src, r * D + part * kEPL, xk);
+    load_src16<SRC>(p.v_src, r * D + part * kEPL, xv);
     if (slot < 0 || slot >= p.num_slots) continue;
-    uint8_t* base = which ? p.v : p.k;
     const int64_t row = slot * hkv + h;
-
-    if constexpr (KIND == kInt8 || KIND == kInt8Inline) {
-      float a = 0.f;
-#pragma unroll
-      for (int i = 0; i < kEPL; ++i) a = fmaxf(a, fabsf(x[i]));
-      a = row_max<kLPR>(a);
-      const float s = a / 127.0f;
-      uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int i = 0; i < kEPL; ++i) {
-        float q = 0.f;
-        if (s != 0.f) q = fminf(fmaxf(rintf(x[i] / s), -127.f), 127.f);
-        w[i >> 2] |= ((uint32_t)(int32_t)q & 0xFFu) << (8 * (i & 3));
-      }
-      if constexpr (KIND == kInt8) {
-        *reinterpret_cast<u32x4*>(base + row * D + part * kEPL) = u32x4{w[0], w[1], w[2], w[3]};
-        if (part == 0) p.kv_scale[row * 2 + which] = s;
-      } else {  // 4-byte-aligned rows of D + 4 bytes
-        uint32_t* dst = reinterpret_cast<uint32_t*>(base + row * (D + 4) + part * kEPL);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = w[i];
-        if (part == 0) *reinterpret_cast<float*>(base + row * (D + 4) + D) = s;
-      }
-    } else if constexpr (KIND == kE4M3) {
-      const float scale = which ? p.v_scale : p.k_scale;
-      uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int i = 0; i < kEPL; ++i) w[i >> 2] |= e4m3_encode(x[i] / scale) << (8 * (i & 3));
-      *reinterpret_cast<u32x4*>(base + row * D + part * kEPL) = u32x4{w[0], w[1], w[2], w[3]};
+    const uint32_t sk = quantize_row<KIND, D>(p, p.k, row, part, 0, xk);
+    const uint32_t sv = quantize_row<KIND, D>(p, p.v, row, part, 1, xv);
+    if constexpr (KIND == kInt8) {
+      if (part == 0) *reinterpret_cast<u32x2*>(p.kv_scale + row * 2) = u32x2{sk, sv};
     } else if constexpr (KIND == kNvfp4) {
-      const float g = which ? p.v_scale : p.k_scale;
-      float a = 0.f;
-#pragma unroll
-      for (int i = 0; i < kEPL; ++i) {   // NaN ignored: a comparison with NaN is false
-        const float v = fabsf(x[i]);     // (a NaN-quieting max could pass a NaN on)
-        a = v > a ? v : a;
-      }
-      const float sb = a / 6.0f;
-      const uint32_t sc = e4m3_encode(sb / g);
-      const float eff = e4m3_value(sc) * g;
-      uint32_t w[2] = {0u, 0u};
-#pragma unroll
-      for (int i = 0; i < kEPL; ++i)
-        w[i >> 3] |= (eff > 0.f ? e2m1_encode(x[i] / eff) : 0u) << (4 * (i & 7));
-      *reinterpret_cast<u32x2*>(base + row * (D / 2) + part * 8) = u32x2{w[0], w[1]};
-      reinterpret_cast<uint8_t*>(p.kv_scale)[(row * 2 + which) * (D / 16) + part] = (uint8_t)sc;
-    } else {  // kBF16: round to nearest even (identity for bf16 sources)
-      uint32_t w[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        bf16x2 b;
-        b[0] = (__bf16)x[2 * i];
-        b[1] = (__bf16)x[2 * i + 1];
-        w[i] = bitcast<uint32_t>(b);
-      }
-      u32x4* dst = reinterpret_cast<u32x4*>(base + row * (2 * D) + part * (2 * kEPL));
-      dst[0] = u32x4{w[0], w[1], w[2], w[3]};
-      dst[1] = u32x4{w[4], w[5], w[6], w[7]};
+      uint8_t* sc = reinterpret_cast<uint8_t*>(p.kv_scale) + row * 2 * (D / 16) + part;
+      sc[0] = (uint8_t)sk;
+      sc[D / 16] = (uint8_t)sv;
     }
   }
 }
@@ -192,7 +216,7 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void kv_write_kernel(WriteP
 template <int KIND, int D>
 hipError_t launch_src(const WriteParams& p, hipStream_t s) {
   constexpr int kRPW = kWave / (D / kEPL);
-  const int64_t groups = 2 * ((p.num_tokens * p.num_kv_heads + kRPW - 1) / kRPW);
+  const int64_t groups = (p.num_tokens * p.num_kv_heads + kRPW - 1) / kRPW;
   const int64_t want = (groups + kWavesPerBlock - 1) / kWavesPerBlock;
   const unsigned grid = (unsigned)(want < (1 << 20) ? want : (1 << 20));
   const dim3 block(kWavesPerBlock * kWave);
