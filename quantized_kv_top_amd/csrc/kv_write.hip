@@ -119,11 +119,24 @@ __device__ __forceinline__ uint32_t quantize_row(const WriteParams& p, uint8_t* 
     for (int i = 0; i < kEPL; ++i) a = fmaxf(a, fabsf(x[i]));
     a = row_max<kLPR>(a);
     const float s = a / 127.0f;
+    // x / s is taken as x * RN(1/s).  |x / s| <= 127 (1 + 2^-24), and the
+    // product is within |x / s| 2^-23 (1 + 2^-25) of the exact quotient, so
+    // within 2^-16 + 2^-18 (its half ulp) of the correctly rounded one: both
+    // round to the same integer unless the product lies within 2^-14 of a
+    // half-integer.  There (and when 1/s overflows) x / s is divided out
+    // exactly.  NaN and +-inf take the same course either way.
+    const float r = 1.0f / s;
+    const bool fast = r <= 3.4028234663852886e38f;
     uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < kEPL; ++i) {
       float q = 0.f;
-      if (s != 0.f) q = fminf(fmaxf(rintf(x[i] / s), -127.f), 127.f);
+      if (s != 0.f) {
+        float y = x[i] * r;
+        const float ay = fabsf(y);
+        if (!fast || fabsf((ay - floorf(ay)) - 0.5f) <= 0x1p-14f) y = x[i] / s;
+        q = fminf(fmaxf(rintf(y), -127.f), 127.f);
+      }
       w[i >> 2] |= ((uint32_t)(int32_t)q & 0xFFu) << (8 * (i & 3));
     }
     if constexpr (KIND == kInt8) {

@@ -90,6 +90,43 @@ def test_write_dtypes_and_special_rows(kind, D, src):
     assert_rows_equal(c, oc, np.arange(NB * BS))
 
 
+@pytest.mark.parametrize("src", ["fp32", "bf16"])
+def test_int8_quotients_at_rounding_ties(src):
+    """Rows whose quotients x / s land on, and within a few ulps of, the
+    half-integers where the int8 rounding decides (ties to even), at
+    non-power-of-two scales: the codes must equal the oracle's fp32
+    quotient-then-round."""
+    rng = np.random.default_rng(77 if src == "fp32" else 78)
+    H, D, T = 2, 128, 96
+    x = np.zeros((T, H, D), np.float32)
+    for t in range(T):
+        for h in range(H):
+            amax = np.float32(rng.uniform(0.3, 3.0) * np.exp2(rng.integers(-20, 20)))
+            if src == "bf16":
+                amax = (torch.tensor([float(amax)]).to(torch.bfloat16).float().numpy()[0])
+            s = np.float32(amax / np.float32(127))
+            k = rng.integers(0, 127, size=D - 1)
+            v = ((k + np.float32(0.5)) * s).astype(np.float32)     # ~ on a tie
+            off = rng.integers(-3, 4, size=D - 1).astype(np.int32)  # a few ulps off
+            v = (v.view(np.int32) + off).view(np.float32)
+            v = np.minimum(v, amax) * rng.choice(np.array([-1, 1], np.float32), size=D - 1)
+            x[t, h, 0] = amax
+            x[t, h, 1:] = v
+    tdt = {"fp32": torch.float32, "bf16": torch.bfloat16}[src]
+    kt = torch.from_numpy(x).to(tdt)
+    vt = torch.from_numpy(-x[::-1].copy()).to(tdt)
+    BS, NB = 16, 8
+    slots = rng.permutation(NB * BS)[:T].astype(np.int64)
+    w = wl.Workload("t", 2 * H, H, D, BS, NB, "bf16", "fp32", src, kt, vt, slots,
+                    torch.zeros(1, 2 * H, D, dtype=torch.bfloat16), np.zeros(1, np.int32),
+                    np.zeros((1, 1), np.int32), np.zeros((1, 1), np.int32), 0.1)
+    say("int8 ties", src)
+    for kind in ("int8", "int8_inline"):
+        c = gpu_write(kind, w)
+        oc = oracle_write(kind, w, None, None)
+        assert_rows_equal(c, oc, np.arange(NB * BS))
+
+
 def _sweep_values():
     exps = np.arange(256, dtype=np.uint32)
     top = np.arange(64, dtype=np.uint32) << np.uint32(17)
