@@ -182,17 +182,61 @@ class Cache:
                                                   self.kv_scale.element_size())
 
 
+def _tensor(name, t, dtypes, shape=None, ndim=None):
+    """Check what the C ABI cannot see: a dense (contiguous) tensor of an
+    accepted dtype and shape (None in ``shape`` = any size).  The device is
+    checked by ``_on_device`` once every argument's metadata has passed."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s: expected a torch.Tensor, got %s" % (name, type(t).__name__))
+    if t.dtype not in dtypes:
+        raise TypeError("%s: dtype %s, expected one of %s" % (name, t.dtype, list(dtypes)))
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError("%s: %d dimensions, expected %d" % (name, t.dim(), ndim))
+    if shape is not None and (t.dim() != len(shape) or
+                              any(w is not None and g != w for g, w in zip(t.shape, shape))):
+        raise ValueError("%s: shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s: must be contiguous" % name)
+
+
+def _on_device(**tensors):
+    """After the metadata checks: every tensor given must be on the GPU."""
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError("%s: must be a CUDA (HIP) device tensor" % name)
+
+
+_QDT = (torch.bfloat16, torch.float16)
+_ODT = (torch.bfloat16, torch.float16, torch.float32)
+
+
 def kv_quant_write(cache, k_src, v_src, slot_mapping, stream=None):
     """Quantize-on-write ``k_src``/``v_src`` [T][Hkv][D] into ``cache`` at
     ``slot_mapping`` [T] (int64; < 0 skips)."""
-    d = cache.desc()
+    shape = (None, cache.num_kv_heads, cache.head_dim)
+    _tensor("k_src", k_src, _ODT, shape)
     T = k_src.shape[0]
+    _tensor("v_src", v_src, (k_src.dtype,), (T,) + shape[1:])
+    _tensor("slot_mapping", slot_mapping, (torch.int64,), (T,))
+    _on_device(k_src=k_src, v_src=v_src, slot_mapping=slot_mapping)
+    d = cache.desc()
     _check(lib().kv_quant_write(ctypes.byref(d), _ptr(k_src), _ptr(v_src), dtype_code(k_src), T,
                                 _ptr(slot_mapping), _stream(stream)), "kv_quant_write")
 
 
-def _args(q, row_seq, block_table, topk_idx, sm_scale, out, lse):
-    R, Hq, _ = q.shape
+def _check_attn(q, row_seq, block_table, topk_idx, out, lse):
+    _tensor("q", q, _QDT, ndim=3)
+    R, Hq, D = q.shape
+    _tensor("out", out, _ODT, (R, Hq, D))
+    _tensor("row_seq", row_seq, (torch.int32,), (R,))
+    _tensor("block_table", block_table, (torch.int32,), ndim=2)
+    _tensor("topk_idx", topk_idx, (torch.int32,), (R, None))
+    if lse is not None:
+        _tensor("lse", lse, (torch.float32,), (R, Hq))
+
+
+def _qsa_args(q, row_seq, block_table, topk_idx, sm_scale, out, lse):
+    R, Hq = q.shape[0], q.shape[1]
     return QsaArgs(q.data_ptr(), dtype_code(q), R, Hq, block_table.shape[0], row_seq.data_ptr(),
                    block_table.data_ptr(), block_table.shape[1], topk_idx.shape[1],
                    topk_idx.data_ptr(), float(sm_scale), dtype_code(out), out.data_ptr(),
@@ -202,8 +246,11 @@ def _args(q, row_seq, block_table, topk_idx, sm_scale, out, lse):
 def qsa_sparse_attn_prefill(cache, q, row_seq, block_table, topk_idx, sm_scale, out, lse=None,
                             stream=None):
     """Single-pass sparse attention; writes ``out`` [R][Hq][D] and ``lse`` [R][Hq]."""
+    _check_attn(q, row_seq, block_table, topk_idx, out, lse)
+    _on_device(q=q, out=out, row_seq=row_seq, block_table=block_table, topk_idx=topk_idx,
+               lse=lse)
+    a = _qsa_args(q, row_seq, block_table, topk_idx, sm_scale, out, lse)
     d = cache.desc()
-    a = _args(q, row_seq, block_table, topk_idx, sm_scale, out, lse)
     _check(lib().qsa_sparse_attn_prefill(ctypes.byref(d), ctypes.byref(a), _stream(stream)),
            "qsa_sparse_attn_prefill")
 
@@ -216,8 +263,13 @@ def qsa_sparse_attn_decode(cache, q, row_seq, block_table, topk_idx, sm_scale, o
                            workspace, lse=None, stream=None):
     """Split-K sparse attention with log-sum-exp merge; ``workspace`` is a
     uint8 device tensor of at least qsa_decode_workspace_bytes(...) bytes."""
+    _check_attn(q, row_seq, block_table, topk_idx, out, lse)
+    if workspace is not None:
+        _tensor("workspace", workspace, (torch.uint8,), ndim=1)
+    _on_device(q=q, out=out, row_seq=row_seq, block_table=block_table, topk_idx=topk_idx,
+               lse=lse, workspace=workspace)
+    a = _qsa_args(q, row_seq, block_table, topk_idx, sm_scale, out, lse)
     d = cache.desc()
-    a = _args(q, row_seq, block_table, topk_idx, sm_scale, out, lse)
     wp = None if workspace is None else ctypes.c_void_p(workspace.data_ptr())
     wb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().qsa_sparse_attn_decode(ctypes.byref(d), ctypes.byref(a), num_splits, wp, wb,
@@ -232,7 +284,12 @@ def kv_calib_stats(x, scale, out, workspace, stream=None):
     """Calibration statistics of the device tensor ``x`` (fp16 / bf16 / fp32,
     contiguous) at the E4M3 ``scale``, written by the library into ``out``
     (a device uint8 tensor of at least sizeof(qkv_calib_result) bytes)."""
-    assert x.is_contiguous() and out.numel() >= ctypes.sizeof(QkvCalibResult)
+    _tensor("x", x, _ODT)
+    _tensor("out", out, (torch.uint8,), ndim=1)
+    if out.numel() < ctypes.sizeof(QkvCalibResult):
+        raise ValueError("out: %d bytes, need %d" % (out.numel(), ctypes.sizeof(QkvCalibResult)))
+    _tensor("workspace", workspace, (torch.uint8,), ndim=1)
+    _on_device(x=x, out=out, workspace=workspace)
     _check(lib().kv_calib_stats(_ptr(x), dtype_code(x), x.numel(), float(scale), _ptr(out),
                                 _ptr(workspace), workspace.numel(), _stream(stream)),
            "kv_calib_stats")
@@ -249,9 +306,16 @@ def qsa_topk_select(scores, row_len, topk, out, workspace=None, stream=None):
     -1 padded lists into ``out`` (device int32 [R][topk]).  ``workspace``: a
     device uint8 tensor of qsa_topk_workspace_bytes(...) bytes when that is
     not 0."""
-    assert scores.dim() == 2 and scores.stride(1) == 1 and out.is_contiguous()
+    if not isinstance(scores, torch.Tensor) or scores.dtype not in _ODT:
+        raise TypeError("scores: expected an fp32 / fp16 / bf16 torch.Tensor")
+    if scores.dim() != 2 or scores.stride(1) != 1:
+        raise ValueError("scores: expected a 2-D tensor with contiguous rows")
     R = scores.shape[0]
-    assert out.shape == (R, topk) and row_len.numel() == R and row_len.is_contiguous()
+    _tensor("row_len", row_len, (torch.int32,), (R,))
+    _tensor("out", out, (torch.int32,), (R, topk))
+    if workspace is not None:
+        _tensor("workspace", workspace, (torch.uint8,), ndim=1)
+    _on_device(scores=scores, row_len=row_len, out=out, workspace=workspace)
     wb = 0 if workspace is None else workspace.numel()
     _check(lib().qsa_topk_select(_ptr(scores), dtype_code(scores), R, scores.stride(0),
                                  _ptr(row_len), topk, _ptr(out), _ptr(workspace), wb,
