@@ -792,25 +792,38 @@ __global__ __launch_bounds__(kWave) void qsa_merge_kernel(AttnParams p) {
       for (int i = 0; i < E; ++i) pre[q][i] = 0.f;
     }
   }
-  float mp = kNegInf, lp = 0.f;
-  if (lane < P) {
-    mp = p.ws_ml[2 * (base + lane)];
-    lp = p.ws_ml[2 * (base + lane) + 1];
+  // the partitions' (max, sum) pairs sit at workgroup-uniform addresses:
+  // every lane reads them (scalar loads) -- no cross-lane reductions
+  const float* ml = p.ws_ml + 2 * base;
+  float mq[kPre], lq[kPre];
+#pragma unroll
+  for (int q = 0; q < kPre; ++q) {
+    mq[q] = kNegInf;
+    lq[q] = 0.f;
+    if (q < P) {                                            // uniform
+      mq[q] = ml[2 * q];
+      lq[q] = ml[2 * q + 1];
+    }
   }
-  const float M = wave_max(mp);
-  const float f = (mp == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(mp - M);
-  const float L = wave_sum(f * lp);
+  float M = kNegInf;
+#pragma unroll
+  for (int q = 0; q < kPre; ++q) M = fmaxf(M, mq[q]);
+  for (int q = kPre; q < P; ++q) M = fmaxf(M, ml[2 * q]);
+  float L = 0.f;
   float acc[E];
 #pragma unroll
   for (int i = 0; i < E; ++i) acc[i] = 0.f;
 #pragma unroll
   for (int q = 0; q < kPre; ++q) {
-    const float fq = __shfl(f, q);
+    const float fq = mq[q] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mq[q] - M);
+    L += fq * lq[q];
 #pragma unroll
     for (int i = 0; i < E; ++i) acc[i] += fq * pre[q][i];
   }
   for (int q = kPre; q < P; ++q) {
-    const float fq = __shfl(f, q);
+    const float mq = ml[2 * q];
+    const float fq = mq == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mq - M);
+    L += fq * ml[2 * q + 1];
 #pragma unroll
     for (int i = 0; i < E; ++i) acc[i] += fq * src[(int64_t)q * D + i];
   }
