@@ -629,8 +629,9 @@ def bench_e2e(args):
     """The end-to-end layer step of one 131K-token sequence in a 13.75 GiB
     pool per cache kind: write an 8192-token chunk (quantize-on-write),
     prefill its 8192 rows with top-k 1024, then 8 decode steps of [write one
-    token, attend with top-k 2048, split-K 8].  Each arm cycles over
-    ``--layers`` (default 2) independent layers, each with its own pool."""
+    token, attend with top-k 2048, split-K 8] (graph-captured).  Each arm
+    cycles over ``--layers`` (default 2) independent layers, each with its
+    own pool."""
     stream = torch.cuda.current_stream()
     L = args.layers or 2
     arms = {}
@@ -646,8 +647,22 @@ def bench_e2e(args):
                               args.warmup, stream)
         pf, _, _ = timed_loop(lambda i: layers[i % L].prefill(stream), args.steps,
                               args.warmup, stream)
-        dc, _, _ = timed_loop(lambda i: layers[i % L].decode_steps(stream), args.steps,
-                              args.warmup, stream)
+        # the decode steps (16 small launches) as one captured graph per layer,
+        # so that host launch overhead stays out of their time
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for lay in layers:
+                lay.decode_steps(side)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = []
+        for lay in layers:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                lay.decode_steps(side)
+            graphs.append(g)
+        dc, _, _ = timed_loop(lambda i: graphs[i % L].replay(), args.steps, args.warmup, stream)
         pf_ms, wr_ms, dc_ms = pf / args.steps, wr / args.steps, dc / args.steps
         pb = R * gathered_bytes_per_row(kind, topk, 2, 256)
         per_tok = sum(qsakv.cache_bytes(kind, 1, 64, 2, 256)) // 64
@@ -664,7 +679,8 @@ def bench_e2e(args):
         }
         log("%s: write %.3f ms, prefill %.3f ms (%.0f GB/s), 8 decode steps %.3f ms" % (
             kind, wr_ms, pf_ms, arms[kind]["chunk_prefill_gathered_GBps"], dc_ms))
-        del layers
+        del graphs, layers
+        torch.cuda.synchronize()
         torch.cuda.empty_cache()
     for kind in arms:
         arms[kind]["pool_tokens_vs_bf16"] = arms[kind]["pool_tokens"] / arms["bf16"]["pool_tokens"]
@@ -676,7 +692,8 @@ def bench_e2e(args):
             "config": {"workload": "e2e: one 131K-token sequence per layer in a 13.75 GiB pool "
                                    "(Hq 16 / Hkv 2, D 256, block 64, bf16 Q/out); 8192-token "
                                    "chunk write + prefill (top-k 1024) + 8 x [write 1 token, "
-                                   "decode top-k 2048, split-K 8]; %d layers rotated; value = "
+                                   "decode top-k 2048, split-K 8] (one graph); %d layers rotated; "
+                                   "value = "
                                    "int8 chunk-prefill rows/s" % L,
                        "arms": arms,
                        "hbm_frac_int8_prefill": a["chunk_prefill_gathered_GBps"] / HBM_PEAK_GBPS}}
