@@ -94,9 +94,12 @@ struct TileRaw {
   u32x4 k[G::kBlk][G::kKChunks];    // tokens 16 b + ln16
   uint32_t v[G::kTok][G::kVWords];  // tokens tok(grp, e)
   float sk[G::kTok], sv[G::kTok];   // int8 scales of tokens tok(grp, e)
-  uint32_t ksc[G::kBlk];            // NVFP4: K block-scale codes of token 16 b + ln16,
-                                    //   byte 2c + i = block 2 grp + 8 c + i
-  uint32_t vsc;                     // NVFP4: byte e = V block-scale code of token tok(grp, e)
+  // NVFP4: K block-scale codes of token 16 b + ln16, chunk c's pair in the
+  // low 16 bits (byte i = block 2 grp + 8 c + i); the V block-scale code of
+  // token tok(grp, e).  Held as loaded: no arithmetic touches a load result
+  // before the tile is computed, so issuing a tile never waits for it.
+  uint32_t ksc[G::kBlk][G::kFp4 ? G::kKChunks : 1];
+  uint32_t vsc[G::kFp4 ? G::kTok : 1];
   uint32_t valid;                   // bit e: token tok(grp, e) is attended
 };
 
@@ -132,13 +135,10 @@ __device__ __forceinline__ void issue_tile(TileRaw<KIND, D, TT>& t, const AttnPa
       // chunk c of this lane holds the codes of blocks 2 grp + 8 c and + 1
       const uint8_t* sr = reinterpret_cast<const uint8_t*>(p.kv_scale) +
                           ((int64_t)(s < 0 ? 0 : s) * hkv + g) * 2 * G::kBlkScales + 2 * grp;
-      uint32_t sc = 0;
 #pragma unroll
-      for (int c = 0; c < G::kKChunks; ++c) sc |= (uint32_t)ld<uint16_t>(sr + 8 * c) << (16 * c);
-      t.ksc[b] = sc;
+      for (int c = 0; c < G::kKChunks; ++c) t.ksc[b][c] = ld<uint16_t>(sr + 8 * c);
     }
   }
-  uint32_t vsc = 0;
   int vs[G::kTok];
   {
     const int4 s0 = *reinterpret_cast<const int4*>(ts + 4 * grp);
@@ -173,20 +173,11 @@ __device__ __forceinline__ void issue_tile(TileRaw<KIND, D, TT>& t, const AttnPa
         t.v[e][4 + i] = w1[i];
       }
     }
-    if constexpr (KIND == kE4M3 || KIND == kBF16) {
-      // a padding token reads row 0; clear its codes so that a NaN stored
-      // there cannot reach the weighted sum (its weight is exactly 0)
-#pragma unroll
-      for (int i = 0; i < G::kVWords; ++i) t.v[e][i] = s < 0 ? 0u : t.v[e][i];
-    }
     if constexpr (G::kFp4) {
-      // the lane's D/16 values of the row form block ln16 * kVBytes / 8; a
-      // padding token's scale is cleared (a NaN scale code stored in row 0
-      // must not reach the weighted sum)
-      const uint8_t* sr = reinterpret_cast<const uint8_t*>(p.kv_scale) +
-                          (rowi * 2 + 1) * G::kBlkScales + ln16 * G::kVBytes / 8;
-      const uint32_t sc = s < 0 ? 0u : (uint32_t)*sr;
-      vsc = e == 0 ? sc : (vsc | (sc << (8 * e)));
+      // the lane's D/16 values of the row form block ln16 * kVBytes / 8
+      // (a padding token reads row 0's; cleared where the tile is computed)
+      t.vsc[e] = reinterpret_cast<const uint8_t*>(p.kv_scale)[(rowi * 2 + 1) * G::kBlkScales +
+                                                               ln16 * G::kVBytes / 8];
     }
     if constexpr (KIND == kInt8) {
       const float2 sc = *reinterpret_cast<const float2*>(p.kv_scale + rowi * 2);
@@ -198,7 +189,6 @@ __device__ __forceinline__ void issue_tile(TileRaw<KIND, D, TT>& t, const AttnPa
     }
   }
   t.valid = valid;
-  if constexpr (G::kFp4) t.vsc = vsc;
 }
 
 struct WaveState {
@@ -269,7 +259,7 @@ __device__ __forceinline__ void compute_tile(const TileRaw<KIND, D, TT>& t, cons
         // step i: word i & 3 of chunk i >> 2 (8 codes), block 2 grp + 8 (i >> 2)
         // + ((i & 3) >> 1); operand = E2M1 value x block scale, exact in fp16
         const uint32_t w = t.k[b][i >> 2][i & 3];
-        const uint32_t scb = (t.ksc[b] >> (16 * (i >> 2) + 8 * ((i & 3) >> 1))) & 0xFFu;
+        const uint32_t scb = (t.ksc[b][i >> 2] >> (8 * ((i & 3) >> 1))) & 0xFFu;
         const f16x2 sc2 = bitcast<f16x2>(e4m3pair_to_f16x2<false>(scb | (scb << 8)));
         u32x4 a;
         a[0] = bitcast<uint32_t>(bitcast<f16x2>(e2m1pair_to_f16x2<0>(w)) * sc2);
@@ -357,6 +347,15 @@ __device__ __forceinline__ void compute_tile(const TileRaw<KIND, D, TT>& t, cons
     for (int j = 0; j < G::kPV; ++j) o[j] *= beta;
   }
   // ---- O^T += V^T W -------------------------------------------------------
+  // A padding token reads row 0: its codes (E4M3, bf16) or its block scale
+  // (NVFP4) are cleared here, so that a NaN stored there cannot reach the
+  // weighted sum (its weight is exactly 0).
+  uint32_t vm[G::kTok][G::kVWords];
+#pragma unroll
+  for (int e = 0; e < G::kTok; ++e)
+#pragma unroll
+    for (int i = 0; i < G::kVWords; ++i)
+      vm[e][i] = (KIND == kE4M3 || KIND == kBF16) && !((t.valid >> e) & 1u) ? 0u : t.v[e][i];
   if constexpr (KIND == kBF16) {
 #pragma unroll
     for (int c = 0; c < G::kVWords; ++c) {
@@ -367,8 +366,8 @@ __device__ __forceinline__ void compute_tile(const TileRaw<KIND, D, TT>& t, cons
 #pragma unroll
         for (int e = 0; e < 4; ++e) bw[e] = (__bf16)w[e];
         u32x2 a;
-        a[0] = perm(t.v[1][c], t.v[0][c], sel);
-        a[1] = perm(t.v[3][c], t.v[2][c], sel);
+        a[0] = perm(vm[1][c], vm[0][c], sel);
+        a[1] = perm(vm[3][c], vm[2][c], sel);
         o[2 * c + hb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bitcast<bf16x4>(a), bw,
                                                                    o[2 * c + hb], 0, 0, 0);
       }
@@ -382,11 +381,14 @@ __device__ __forceinline__ void compute_tile(const TileRaw<KIND, D, TT>& t, cons
     f16x4 bw;
 #pragma unroll
     for (int e = 0; e < 4; ++e) bw[e] = (_Float16)w[e];
-    const f16x2 sc01 = bitcast<f16x2>(e4m3pair_to_f16x2<false>(t.vsc));
-    const f16x2 sc23 = bitcast<f16x2>(e4m3pair_to_f16x2<true>(t.vsc));
+    uint32_t vs[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vs[e] = ((t.valid >> e) & 1u) ? t.vsc[e] : 0u;
+    const f16x2 sc01 = bitcast<f16x2>(e4m3pair_to_f16x2<false>(perm(vs[1], vs[0], 0x0C0C0400u)));
+    const f16x2 sc23 = bitcast<f16x2>(e4m3pair_to_f16x2<false>(perm(vs[3], vs[2], 0x0C0C0400u)));
 #pragma unroll
     for (int c = 0; c < G::kVWords; ++c) {
-      const uint32_t w0 = t.v[0][c], w1 = t.v[1][c], w2 = t.v[2][c], w3 = t.v[3][c];
+      const uint32_t w0 = vm[0][c], w1 = vm[1][c], w2 = vm[2][c], w3 = vm[3][c];
       const uint32_t x01[2] = {(w0 & 0x0F0F0F0Fu) | ((w1 << 4) & 0xF0F0F0F0u),    // low nibbles
                                ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u)};  // high nibbles
       const uint32_t x23[2] = {(w2 & 0x0F0F0F0Fu) | ((w3 << 4) & 0xF0F0F0F0u),
@@ -413,7 +415,7 @@ __device__ __forceinline__ void compute_tile(const TileRaw<KIND, D, TT>& t, cons
     for (int c = 0; c < G::kVWords; ++c) {
       uint32_t tk[NT / 2][2];
 #pragma unroll
-      for (int k = 0; k < NT / 2; ++k) interleave_pair<KIND>(t.v[2 * k][c], t.v[2 * k + 1][c], tk[k]);
+      for (int k = 0; k < NT / 2; ++k) interleave_pair<KIND>(vm[2 * k][c], vm[2 * k + 1][c], tk[k]);
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) {
         f16x4 bw;
