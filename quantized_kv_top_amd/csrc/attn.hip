@@ -462,7 +462,7 @@ __device__ __forceinline__ void store_row(void* out, int out_dtype, int64_t off,
   }
 }
 
-template <int KIND, int D, int TT, int NW>
+template <int KIND, int D, int TT, int NW, bool kMulti>
 __device__ __forceinline__ void attn_body(const AttnParams& p) {
   using G = Geo<KIND, D, TT>;
   constexpr int kThreads = NW * kWave;
@@ -638,23 +638,45 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
 #pragma unroll
   for (int j = 0; j < G::kPV; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int c0 = 0; c0 < npos; c0 += kChunk) {
-    if (c0 > 0) {
-      __syncthreads();               // the previous chunk's slots are consumed
-      chunk_start(c0);
-      chunk_finish(c0);
-      __syncthreads();
-      my_n = wave_tiles(c0);
-      if (my_n > 0) issue_tile<KIND, D, TT>(ta, p, g, ts(0));
-      if (my_n > 1) issue_tile<KIND, D, TT>(tb, p, g, ts(1));
-    }
-    for (int k = 0; k < my_n; k += 2) {
+  // Tiles k (in ta) and k + 1 (in tb) are in flight at the top of each
+  // pass.  The steady passes issue both successors unconditionally, so a
+  // tile's loads land straight in the registers the next pass reads; the
+  // last one to three tiles are finished after the loop.
+  auto tile_loop = [&]() {
+    int k = 0;
+    for (; k + 3 < my_n; k += 2) {
       compute_tile<KIND, D, TT, QS>(ta, qs, kfac, kbias, st, o);
-      if (k + 2 < my_n) issue_tile<KIND, D, TT>(ta, p, g, ts(k + 2));
-      if (k + 1 < my_n) {
-        compute_tile<KIND, D, TT, QS>(tb, qs, kfac, kbias, st, o);
-        if (k + 3 < my_n) issue_tile<KIND, D, TT>(tb, p, g, ts(k + 3));
+      issue_tile<KIND, D, TT>(ta, p, g, ts(k + 2));
+      compute_tile<KIND, D, TT, QS>(tb, qs, kfac, kbias, st, o);
+      issue_tile<KIND, D, TT>(tb, p, g, ts(k + 3));
+    }
+    const int r = my_n - k;                                 // 0 .. 3 tiles left
+    if (r > 0) {
+      compute_tile<KIND, D, TT, QS>(ta, qs, kfac, kbias, st, o);
+      if (r > 2) issue_tile<KIND, D, TT>(ta, p, g, ts(k + 2));
+    }
+    if (r > 1) compute_tile<KIND, D, TT, QS>(tb, qs, kfac, kbias, st, o);
+    if (r > 2) compute_tile<KIND, D, TT, QS>(ta, qs, kfac, kbias, st, o);
+  };
+  // Partitions that fit one LDS chunk of slots (kMulti false: chosen by the
+  // host from the partition size) run the tile loop alone; with no chunk
+  // loop around it the compiler follows the two tiles in flight across its
+  // back edge and waits for each tile's loads as they are used rather than
+  // for all loads outstanding.
+  if constexpr (!kMulti) {
+    tile_loop();
+  } else {
+    for (int c0 = 0; c0 < npos; c0 += kChunk) {
+      if (c0 > 0) {
+        __syncthreads();               // the previous chunk's slots are consumed
+        chunk_start(c0);
+        chunk_finish(c0);
+        __syncthreads();
+        my_n = wave_tiles(c0);
+        if (my_n > 0) issue_tile<KIND, D, TT>(ta, p, g, ts(0));
+        if (my_n > 1) issue_tile<KIND, D, TT>(tb, p, g, ts(1));
       }
+      tile_loop();
     }
   }
 
@@ -758,10 +780,10 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
 }
 
 // 16-token tiles at two waves per SIMD (<= 256 registers per wave).
-template <int KIND, int D, int NW>
+template <int KIND, int D, int NW, bool kMulti>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void qsa_attn16_kernel(AttnParams p) {
-  attn_body<KIND, D, 16, NW>(p);
+  attn_body<KIND, D, 16, NW, kMulti>(p);
 }
 
 // Log-sum-exp merge of the split-K partials of one (row, head) per wave:
@@ -856,7 +878,12 @@ __global__ __launch_bounds__(kWave) void qsa_merge_kernel(AttnParams p) {
 // 1024, 1 up to 2048).  Large launches (prefill) keep 4 waves per item.
 template <int KIND, int D, int NW>
 hipError_t launch_knw(const AttnParams& p, unsigned grid, hipStream_t s) {
-  qsa_attn16_kernel<KIND, D, NW><<<grid, dim3(NW * kWave), 0, s>>>(p);
+  // slots resolved per LDS batch by an NW-wave workgroup (attn_body's kChunk)
+  constexpr int kChunk = pos_per_thread<NW>() * NW * kWave;
+  if (p.chunk <= kChunk)
+    qsa_attn16_kernel<KIND, D, NW, false><<<grid, dim3(NW * kWave), 0, s>>>(p);
+  else
+    qsa_attn16_kernel<KIND, D, NW, true><<<grid, dim3(NW * kWave), 0, s>>>(p);
   return hipGetLastError();
 }
 
