@@ -109,6 +109,34 @@ def test_workgroup_shapes(kind, D):
         check(o, l, ro, rl, "wg shapes %s D%d P%d" % (kind, D, P))
 
 
+# (waves per workgroup, rows, positions one workgroup resolves per LDS batch):
+# with 8 KV heads the rows give 32, 520, 1040 and 2056 workgroup items, one
+# for each wave count the launch picks by item count.
+_SHAPES = [(8, 4, 1024), (2, 65, 512), (1, 130, 256), (4, 257, 1024)]
+
+
+@pytest.mark.parametrize("nw,rows,batch", _SHAPES, ids=["nw%d" % s[0] for s in _SHAPES])
+@pytest.mark.parametrize("extra", [0, 1, "2x"])
+def test_list_length_at_lds_batch_edges(nw, rows, batch, extra):
+    """A row's list exactly one LDS batch of positions long, one position
+    longer, and a little over two batches: the single-batch and the batched
+    tile loops meet at these lengths, for every workgroup shape.  The list
+    carries 3 padding entries; large launches are checked on sampled rows."""
+    width = batch + (batch + 37 if extra == "2x" else extra)
+    kinds = ["int8", "nvfp4"] if extra == 1 else ["int8"]
+    w = small_workload(seed=41 + nw, Hq=8, Hkv=8, D=128, ctx=width + rows + 3, rows=rows,
+                       topk=width - 3, pad=3)
+    assert w.topk_idx.shape[1] == width
+    rng = np.random.default_rng(nw)
+    pick = np.unique(np.concatenate([[0, rows - 1], rng.integers(0, rows, 10)]))
+    for kind in kinds:
+        c, oc = _setup(kind, w)
+        ro, rl = oracle_attention(oc, w, rows=pick)
+        say("lds batch edge", kind, "nw", nw, "rows", rows, "width", width)
+        o, l = run_attention(c, w)
+        check(o[pick], l[pick], ro, rl, "batch edge %s nw%d width %d" % (kind, nw, width))
+
+
 @pytest.mark.parametrize("G", [1, 4, 16])
 def test_group_sizes(G):
     w = small_workload(seed=13, Hq=2 * G, Hkv=2, D=128, topk=40)
