@@ -161,7 +161,7 @@ typedef struct qsa_args {
   const int32_t *row_seq;        /* device [R]: sequence of each row         */
   const int32_t *block_table;    /* device [B][block_table_stride]           */
   int32_t block_table_stride;    /* >= 1 (max blocks per sequence)           */
-  int32_t topk;                  /* >= 1                                     */
+  int32_t topk;                  /* 1 .. 2^30                                */
   const int32_t *topk_idx;       /* device [R][topk] logical positions       */
   float sm_scale;                /* finite softmax scale (e.g. 1/sqrt(D))    */
   int32_t out_dtype;             /* QKV_BF16, QKV_FP16 or QKV_FP32           */
@@ -353,8 +353,8 @@ QSAKV_API int32_t qkv_abi_version(void);
  *   q dtype               bf16 or fp16; BF16 caches need bf16 queries
  *   out dtype             bf16, fp16, fp32
  *   src dtype (writes)    fp32, bf16, fp16
- * Sizes must keep every tensor below 2^63 bytes and R * Hq, R * topk below
- * 2^31 (else QKV_ERR_BAD_SHAPE).
+ * Sizes must keep every tensor below 2^63 bytes, R * Hq and R * topk below
+ * 2^31, and the attention calls' topk at most 2^30 (else QKV_ERR_BAD_SHAPE).
  */
 
 #ifdef __cplusplus

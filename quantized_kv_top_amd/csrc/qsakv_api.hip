@@ -109,8 +109,9 @@ qkv_status finish(hipError_t e) {
 
 qkv_status check_args(const qkv_cache* c, const qsa_args* a) {
   if (!a) return QKV_ERR_NULL;
+  // topk <= 2^30 keeps ceil(topk / P) * P and every partition's end within int32
   if (a->num_rows < 0 || a->num_q_heads <= 0 || a->num_seqs <= 0 || a->block_table_stride <= 0 ||
-      a->topk <= 0)
+      a->topk <= 0 || a->topk > (1 << 30))
     return QKV_ERR_BAD_SHAPE;
   if (a->num_q_heads % c->num_kv_heads != 0) return QKV_ERR_BAD_SHAPE;
   const int group = a->num_q_heads / c->num_kv_heads;

@@ -105,6 +105,8 @@ def test_shapes_and_supported_set():
     assert _prefill(_cache(H=3), _args(Hq=4)) == qsakv.ERR_BAD_SHAPE
     assert _prefill(_cache(H=1), _args(Hq=32)) == qsakv.ERR_UNSUPPORTED
     assert _prefill(_cache(), _args(topk=0)) == qsakv.ERR_BAD_SHAPE
+    assert _prefill(_cache(), _args(R=1, topk=(1 << 30) + 1)) == qsakv.ERR_BAD_SHAPE
+    assert _decode(_cache(), _args(R=1, topk=(1 << 31) - 1)) == qsakv.ERR_BAD_SHAPE
     assert _prefill(_cache(), _args(R=-1)) == qsakv.ERR_BAD_SHAPE
     assert _prefill(_cache(), _args(q_dtype=qsakv.FP32)) == qsakv.ERR_UNSUPPORTED
     assert _prefill(_cache(kind="bf16"), _args(q_dtype=qsakv.FP16)) == qsakv.ERR_UNSUPPORTED
