@@ -635,7 +635,7 @@ def bench_e2e(args):
     stream = torch.cuda.current_stream()
     L = args.layers or 2
     arms = {}
-    for kind in ("int8", "bf16", "e4m3", "nvfp4"):
+    for kind in ("int8", "int8_inline", "bf16", "e4m3", "nvfp4"):
         log("building %d e2e layers (%s)" % (L, kind))
         layers = [E2ELayer(kind, 5 + 100 * i) for i in range(L)]
         for lay in layers:       # the step's inputs are device-resident before timing
@@ -696,6 +696,8 @@ def bench_e2e(args):
                                    "value = "
                                    "int8 chunk-prefill rows/s" % L,
                        "arms": arms,
+                       "inline260_over_aligned_prefill": arms["int8_inline"]["chunk_prefill_ms"]
+                       / a["chunk_prefill_ms"],
                        "hbm_frac_int8_prefill": a["chunk_prefill_gathered_GBps"] / HBM_PEAK_GBPS}}
 
 
