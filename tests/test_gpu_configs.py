@@ -96,7 +96,7 @@ def test_mixed_catch_up_and_decode_rows_one_launch():
         check(o, l, ro, rl, "mixed P%d" % P)
 
 
-@pytest.mark.parametrize("kind", ["int8", "e4m3", "bf16", "nvfp4"])
+@pytest.mark.parametrize("kind", ["int8", "int8_inline", "e4m3", "bf16", "nvfp4"])
 def test_e2e_layer_step(kind):
     """Existing context + an 8192-token chunk written (quantize-on-write) and
     attended with top-k 1024, then 8 decode steps of one new token each with
