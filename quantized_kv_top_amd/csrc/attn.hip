@@ -796,7 +796,16 @@ __global__ __launch_bounds__(kWave) void qsa_merge_kernel(AttnParams p) {
   constexpr int E = D / kWave;
   constexpr int kPre = 8;
   const int lane = lane_id();
-  const int64_t rh = blockIdx.x;   // r * Hq + h
+  // (row, query head) r * Hq + h; consecutive ones share an XCD, in the same
+  // split as the attention launch's items, so that a head's partials are
+  // mostly read on the XCD whose L2 holds them
+  int64_t rh;
+  {
+    const int n = p.num_rows * p.num_q_heads;
+    const int b = blockIdx.x, x = b & 7, k = b >> 3;
+    const int q8 = n >> 3, rem = n & 7;
+    rh = x * q8 + (x < rem ? x : rem) + k;
+  }
   const int P = p.num_splits;
   const int64_t base = rh * P;
   const float* src = p.ws_o + base * D + lane * E;
