@@ -31,12 +31,16 @@
 //
 // Exact operands.  E4M3 codes become fp16 through gfx950's OCP-FP8 convert.
 // An int8 code q becomes the fp16 value 1152 + q (0x64 in the high byte and
-// q + 128 in the low byte -- exact, one byte permute per pair); the constant
-// 1152 is removed after the MFMA: from each logit as 1152 * sum_d q'_d, and
-// from the output as 1152 * sum_t W_t, both sums of exactly what entered the
-// MFMA.  Queries are rounded to fp16 after an exact power-of-two prescale;
-// bf16 caches run bf16 MFMA directly (their query operand staged in LDS at
-// D = 256, where the registers go to the tiles in flight).
+// q + 128 in the low byte -- exact, one byte permute per pair).  K operands
+// then have the 1152 subtracted in fp16 (exact), so the logits accumulate
+// the products q * Q alone.  V operands keep it: it is removed from the
+// output after the MFMA as 1152 * sum_t W_t (the sum of exactly the weights
+// that entered the MFMA); in value units the offset is 1152 * s_v ~ 9
+// max|v|, so its share of the fp32 accumulation error stays ~2^-21 max|v|
+// per accumulation step.  Queries are rounded to fp16 after an exact
+// power-of-two prescale; bf16 caches run bf16 MFMA directly (their query
+// operand staged in LDS at D = 256, where the registers go to the tiles in
+// flight).
 //
 // Scales.  The int8 per-token K scale multiplies the logit after the dot
 // product; the per-token V scale enters the softmax weight
@@ -239,7 +243,7 @@ __device__ __forceinline__ uint32_t v_pair_f16(const uint32_t (&tk)[2], int bb) 
 
 template <int KIND, int D, int TT, typename QS>
 __device__ __forceinline__ void compute_tile(const TileRaw<KIND, D, TT>& t, const QS& q,
-                                             float kfac, float kbias, WaveState& st,
+                                             float kfac, WaveState& st,
                                              f32x4 (&o)[Geo<KIND, D, TT>::kPV]) {
   using G = Geo<KIND, D, TT>;
   constexpr int NT = G::kTok;
@@ -277,11 +281,15 @@ __device__ __forceinline__ void compute_tile(const TileRaw<KIND, D, TT>& t, cons
           a[2] = e4m3pair_to_f16x2<false>(w1);
           a[3] = e4m3pair_to_f16x2<true>(w1);
         } else {
+          // 1152 + q by byte permute, then the 1152 taken off in fp16 (exact
+          // for every code): the operand is q itself, so each logit's
+          // accumulation error scales with its own products and not with
+          // 1152 times the query's sum over the head dimension
           const uint32_t x0 = w0 ^ 0x80808080u, x1 = w1 ^ 0x80808080u;
-          a[0] = i8pair_to_f16x2(x0, kSelB01);
-          a[1] = i8pair_to_f16x2(x0, kSelB23);
-          a[2] = i8pair_to_f16x2(x1, kSelB01);
-          a[3] = i8pair_to_f16x2(x1, kSelB23);
+          a[0] = i8pair_unbias(i8pair_to_f16x2(x0, kSelB01));
+          a[1] = i8pair_unbias(i8pair_to_f16x2(x0, kSelB23));
+          a[2] = i8pair_unbias(i8pair_to_f16x2(x1, kSelB01));
+          a[3] = i8pair_unbias(i8pair_to_f16x2(x1, kSelB23));
         }
         s[b] = mfma16(bitcast<f16x8>(a), q[i], s[b]);
       }
@@ -292,12 +300,9 @@ __device__ __forceinline__ void compute_tile(const TileRaw<KIND, D, TT>& t, cons
   float mx = kNegInf;
 #pragma unroll
   for (int e = 0; e < NT; ++e) {
-    float raw = s[e >> 2][e & 3];
+    const float raw = s[e >> 2][e & 3];
     float f = kfac;
-    if constexpr (G::kInt) {
-      raw -= kbias;
-      f *= t.sk[e];
-    }
+    if constexpr (G::kInt) f *= t.sk[e];
     y[e] = ((t.valid >> e) & 1u) ? raw * f : kNegInf;
     mx = fmaxf(mx, y[e]);
   }
@@ -333,8 +338,11 @@ __device__ __forceinline__ void compute_tile(const TileRaw<KIND, D, TT>& t, cons
 #pragma unroll
     for (int e = 0; e < NT; ++e) {
       // the weight as it enters the MFMA (fp16), so that the bias removed
-      // afterwards is exactly the one the MFMA added
-      w[e] = (float)(_Float16)(pr[e] * (t.sv[e] * rs));
+      // afterwards is exactly the one the MFMA added.  A padding token reads
+      // row 0's scale: it is replaced by 0 (a NaN or inf stored there would
+      // otherwise turn the zero weight into NaN).
+      const float sv = ((t.valid >> e) & 1u) ? t.sv[e] : 0.f;
+      w[e] = (float)(_Float16)(pr[e] * (sv * rs));
       wsum += w[e];
     }
     st.cw = st.cw * beta + wsum;
@@ -568,7 +576,7 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
 
   // ---- Q operand (B of QK^T), the logit factor and the int8 bias term ----
   QOp<KIND> qop[G::kQK];
-  float kfac, kbias = 0.f;
+  float kfac;
   if constexpr (KIND == kBF16) {
 #pragma unroll
     for (int i = 0; i < G::kQK; ++i) qop[i] = bitcast<bf16x8>(qraw[i]);
@@ -608,14 +616,6 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
       }
     }
     kfac = p.sm_log2e * p.k_scale * ldexpf(1.f, -e);
-    if constexpr (G::kInt) {
-      float qs = 0.f;
-#pragma unroll
-      for (int i = 0; i < G::kQK; ++i)
-#pragma unroll
-        for (int k = 0; k < 8; ++k) qs += (float)qop[i][k];
-      kbias = kI8Bias * group4_sum(qs);
-    }
   }
 
   using QS = std::conditional_t<G::kQLds, QLds<KIND>, QRegs<KIND, G::kQK>>;
@@ -645,18 +645,18 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
   auto tile_loop = [&]() {
     int k = 0;
     for (; k + 3 < my_n; k += 2) {
-      compute_tile<KIND, D, TT, QS>(ta, qs, kfac, kbias, st, o);
+      compute_tile<KIND, D, TT, QS>(ta, qs, kfac, st, o);
       issue_tile<KIND, D, TT>(ta, p, g, ts(k + 2));
-      compute_tile<KIND, D, TT, QS>(tb, qs, kfac, kbias, st, o);
+      compute_tile<KIND, D, TT, QS>(tb, qs, kfac, st, o);
       issue_tile<KIND, D, TT>(tb, p, g, ts(k + 3));
     }
     const int r = my_n - k;                                 // 0 .. 3 tiles left
     if (r > 0) {
-      compute_tile<KIND, D, TT, QS>(ta, qs, kfac, kbias, st, o);
+      compute_tile<KIND, D, TT, QS>(ta, qs, kfac, st, o);
       if (r > 2) issue_tile<KIND, D, TT>(ta, p, g, ts(k + 2));
     }
-    if (r > 1) compute_tile<KIND, D, TT, QS>(tb, qs, kfac, kbias, st, o);
-    if (r > 2) compute_tile<KIND, D, TT, QS>(ta, qs, kfac, kbias, st, o);
+    if (r > 1) compute_tile<KIND, D, TT, QS>(tb, qs, kfac, st, o);
+    if (r > 2) compute_tile<KIND, D, TT, QS>(ta, qs, kfac, st, o);
   };
   // Partitions that fit one LDS chunk of slots (kMulti false: chosen by the
   // host from the partition size) run the tile loop alone; with no chunk

@@ -79,6 +79,12 @@ __device__ __forceinline__ uint32_t i8pair_to_f16x2(uint32_t x_biased, uint32_t 
 }
 constexpr uint32_t kSelB01 = 0x04010400u;  // bytes 0,1 -> (0x64b0, 0x64b1)
 constexpr uint32_t kSelB23 = 0x04030402u;  // bytes 2,3 -> (0x64b2, 0x64b3)
+// (1152 + q_lo, 1152 + q_hi) -> (q_lo, q_hi): one packed fp16 subtract,
+// exact (both operands and the difference are integers below 2^11).
+__device__ __forceinline__ uint32_t i8pair_unbias(uint32_t h) {
+  const f16x2 b = {(_Float16)1152.f, (_Float16)1152.f};
+  return bitcast<uint32_t>(bitcast<f16x2>(h) - b);
+}
 
 // Two OCP E4M3FN codes in the low (hi_word = false) or high 16 bits of w ->
 // two exact fp16 values (every E4M3 value is representable in fp16), using

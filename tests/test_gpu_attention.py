@@ -226,6 +226,63 @@ def test_edge_cases():
     check(o, l, ro, rl, "bad block table")
 
 
+def _without_block0(w):
+    """Move whatever uses physical block 0 to an unused block, so that slot 0
+    (the row every padding token reads) is never attended."""
+    used = set(np.unique(w.block_table).tolist())
+    spare = next(b for b in range(1, w.num_blocks) if b not in used)
+    bt = w.block_table.copy()
+    bt[bt == 0] = spare
+    blk = w.slot_mapping // w.block_size
+    w.slot_mapping = np.where(blk == 0, spare, blk) * w.block_size + w.slot_mapping % w.block_size
+    w.block_table = bt
+    return w
+
+
+def _poison_slot0(c):
+    """NaN / inf in everything slot 0 holds: int8 scales (side tensor and
+    inline slot), E4M3 NaN codes, bf16 NaNs, NVFP4 NaN block-scale codes."""
+    H, D = c.num_kv_heads, c.head_dim
+    bad = np.array([np.nan, np.inf, -np.inf, np.nan][:H] + [np.nan] * max(0, H - 4), np.float32)
+    if c.kind == "int8":
+        c.kv_scale.view(c.num_slots, H, 2)[0] = dev(np.stack([bad, bad[::-1]], axis=1))
+    elif c.kind == "int8_inline":
+        for t in (c.k, c.v):
+            t.view(c.num_slots, H, D + 4)[0, :, D:] = dev(bad.view(np.uint8).reshape(H, 4))
+    elif c.kind == "e4m3":
+        c.k.view(c.num_slots, H, D)[0] = 0x7F
+        c.v.view(c.num_slots, H, D)[0] = 0xFF
+    elif c.kind == "bf16":
+        nan = np.tile(np.array([0xC0, 0x7F], np.uint8), (H, D))   # bf16 NaN 0x7FC0
+        c.k.view(c.num_slots, H, 2 * D)[0] = dev(nan)
+        c.v.view(c.num_slots, H, 2 * D)[0] = dev(nan)
+    elif c.kind == "nvfp4":
+        c.kv_scale.view(c.num_slots, H, 2 * (D // 16))[0] = 0x7F
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_padding_never_reads_slot0_values(kind):
+    """Padding entries (-1, positions past the block table, rows of an
+    invalid sequence) and the padded tail of the last tile read slot 0 as a
+    stand-in; NaN / inf stored there must not reach any output, for lists of
+    every tile phase, at P = 1 and P = 8."""
+    w = _without_block0(small_workload(seed=47, topk=133, rows=10, pad=15))
+    c, oc = _setup(kind, w)
+    _poison_slot0(c)
+    idx = w.topk_idx.copy()
+    idx[0] = -1                                   # an empty row
+    idx[1, 1:] = -1                               # one position, 15 pads in its tile
+    idx[2, :7] = 10 ** 6                          # beyond the block table
+    ref_idx = idx.copy()
+    ref_idx[2, :7] = -1
+    for P in (1, 8):
+        say("padding vs poisoned slot 0", kind, "P", P)
+        o, l = run_attention(c, w, num_splits=P, decode=P > 1, topk_idx=idx)
+        assert np.isfinite(o).all(), "non-finite output"
+        ro, rl = oracle_attention(oc, w, topk_idx=ref_idx)
+        check(o, l, ro, rl, "poisoned slot 0 %s P%d" % (kind, P))
+
+
 def test_equal_keys_give_uniform_softmax():
     """Closed form through the whole HIP path: identical keys -> the output is
     the mean of the selected values."""
@@ -262,6 +319,60 @@ def test_zero_value_rows_and_large_queries():
     o, l = run_attention(c, w, out_dtype="fp32", sm_scale=w.sm_scale * 1e-3)
     ro, rl = oracle_attention(oc, w, sm_scale=w.sm_scale * 1e-3)
     check(o, l, ro, rl, "zero V / large q")
+
+
+def outlier_logit_workload(seed, rows=48, topk=1024, ctx=4096, q_mean=0.75, q_out=5.0,
+                           k_out=30.0):
+    """The prefill layer shape (Hq 16 / Hkv 2, D 256, block 64) with K rows
+    dominated by 4 outlier channels (N(0,1) x ``k_out``) and queries of mean
+    ``q_mean`` whose outlier channels carry +-``q_out``: per-head logits that
+    reach 20-80, set mostly by one or two channels of each key, with a large
+    sum of the query over the head dimension."""
+    rng = np.random.default_rng(seed)
+    Hq, Hkv, D, BS = 16, 2, 256, 64
+    nb = ctx // BS
+    bt = wl.scattered_block_table(rng, 1, nb, nb + 13).astype(np.int32)
+    slots = wl.slot_mapping_for(bt, 0, np.arange(ctx), BS)
+    chans = np.sort(rng.permutation(D)[:4])
+    k = wl.normal((ctx, Hkv, D), seed + 1, "cpu")
+    k[:, :, chans] *= k_out
+    v = wl.normal((ctx, Hkv, D), seed + 2, "cpu")
+    q = wl.normal((rows, Hq, D), seed + 3, "cpu") + q_mean
+    sign = torch.from_numpy(rng.choice([-1.0, 1.0], size=(rows, Hq, 4)).astype(np.float32))
+    q[:, :, chans] = q_out * sign
+    idx = np.stack([wl.draw_sorted_distinct(rng, topk, 0, ctx - rows + r)
+                    for r in range(rows)]).astype(np.int32)
+    return wl.Workload("outlier-logits", Hq, Hkv, D, BS, nb + 13, "bf16", "bf16", "bf16",
+                       k.to(torch.bfloat16), v.to(torch.bfloat16), slots, q.to(torch.bfloat16),
+                       np.zeros(rows, np.int32), bt, idx, wl.sm_scale_for(D))
+
+
+@pytest.mark.parametrize("kind", ["int8", "int8_inline"])
+def test_int8_large_logits_outlier_keys(kind):
+    """Large logits from outlier-dominated int8 keys and nonzero-mean
+    queries: each logit must keep the accuracy of its own products (a
+    constant offset on the codes, times the query's sum over the head
+    dimension, must not set the rounding error).  Prefill and split-K 8, at
+    the stated tolerance; the workload's logits are checked to reach the
+    20-80 range so that the case is the one meant."""
+    w = outlier_logit_workload(53)
+    c, oc = _setup(kind, w)
+    # the oracle's logits of a few rows: the case must reach 20-80
+    qn = w.q.float().numpy().astype(np.float64)
+    top = []
+    for r in range(0, w.num_rows, 8):
+        sl = w.block_table[0][w.topk_idx[r] // 64].astype(np.int64) * 64 + w.topk_idx[r] % 64
+        kh = oc.dequant(sl, "k")                                  # [topk][Hkv][D]
+        lg = np.einsum("hd,thd->ht", qn[r], np.repeat(kh, 8, axis=1)) * w.sm_scale
+        top.append(lg.max(axis=1))
+    top = np.concatenate(top)
+    say("outlier logits: per-head max logit %.1f .. %.1f" % (top.min(), top.max()))
+    assert top.max() >= 60 and np.median(top) >= 20
+    ro, rl = oracle_attention(oc, w)
+    for P in (1, 8):
+        o, l = run_attention(c, w, num_splits=P, decode=P > 1)
+        m = check(o, l, ro, rl, "outlier logits %s P%d" % (kind, P))
+        say("outlier logits", kind, "P", P, m)
 
 
 def test_every_e4m3_code_decodes_exactly():
