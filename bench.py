@@ -407,9 +407,9 @@ def bench_e4m3(args):
 
 
 class MixedLayer:
-    """An E4M3 layer read by a 46 + 1 + 1 + 1 row batch: either in one launch
-    or, as a row-routing reference, as two launches (the 46-row catch-up
-    chunk, then the three decode rows)."""
+    """An E4M3 layer attended by 49 rows (46 + 1 + 1 + 1) either in one
+    launch or, as the row-routing reference, in two launches (rows 0-45,
+    then rows 46-48)."""
 
     def __init__(self, layer, seed, splits):
         w = wl.mixed_layer(layer, device="cuda", seed=seed)
@@ -454,9 +454,11 @@ class _Fn:
 
 
 def bench_mixed(args):
-    """12 E4M3 layers, each read by a mixed batch of a 46-row catch-up chunk
-    plus three decode rows (the last with a shorter list), split-K
-    ``--splits``; one launch per layer vs the two-launch row routing."""
+    """12 E4M3 layers; each layer is attended by one batch of 49 rows (46 rows
+    of one sequence's chunk, then one row from each of three other
+    sequences, the last with a shorter list), split-K ``--splits``; the
+    batch as one launch per layer against the same rows routed as two
+    launches."""
     L = 12
     sets = args.layers or 2
     log("building %d x %d mixed-batch layers" % (L, sets))

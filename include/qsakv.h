@@ -163,7 +163,8 @@ typedef struct qsa_args {
   int32_t block_table_stride;    /* >= 1 (max blocks per sequence)           */
   int32_t topk;                  /* 1 .. 2^30                                */
   const int32_t *topk_idx;       /* device [R][topk] logical positions       */
-  float sm_scale;                /* finite softmax scale (e.g. 1/sqrt(D))    */
+  float sm_scale;                /* softmax scale, finite and > 0 (e.g.
+                                    1/sqrt(D)); else QKV_ERR_BAD_SCALE       */
   int32_t out_dtype;             /* QKV_BF16, QKV_FP16 or QKV_FP32           */
   void *out;                     /* device [R][Hq][D], 16-B aligned          */
   float *lse;                    /* device [R][Hq] natural-log LSE, or NULL  */

@@ -120,7 +120,8 @@ qkv_status check_args(const qkv_cache* c, const qsa_args* a) {
   if (c->kind == QKV_CACHE_BF16 && a->q_dtype != QKV_BF16) return QKV_ERR_UNSUPPORTED;
   if (a->out_dtype != QKV_BF16 && a->out_dtype != QKV_FP16 && a->out_dtype != QKV_FP32)
     return QKV_ERR_UNSUPPORTED;
-  if (!std::isfinite(a->sm_scale)) return QKV_ERR_BAD_SCALE;
+  // the softmax scale must be finite and positive (as the header states)
+  if (!std::isfinite(a->sm_scale) || !(a->sm_scale > 0.f)) return QKV_ERR_BAD_SCALE;
   int64_t t;
   if (!mul_ok(a->num_rows, a->num_q_heads, &t) || t > INT32_MAX) return QKV_ERR_BAD_SHAPE;
   if (!mul_ok(a->num_rows, a->topk, &t) || t > INT32_MAX) return QKV_ERR_BAD_SHAPE;

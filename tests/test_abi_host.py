@@ -124,7 +124,11 @@ def test_fail_closed_scales():
         assert _prefill(_cache("e4m3", ks=ks), _args()) == qsakv.ERR_BAD_SCALE
         assert _prefill(_cache("e4m3", vs=ks), _args()) == qsakv.ERR_BAD_SCALE
         assert _write(_cache("e4m3", ks=ks)) == qsakv.ERR_BAD_SCALE
-    assert _prefill(_cache(), _args(sm=float("nan"))) == qsakv.ERR_BAD_SCALE
+    # the softmax scale: finite and positive (a zero, negative or -0 scale fails)
+    for sm in [float("nan"), float("inf"), -float("inf"), 0.0, -0.0, -0.0625]:
+        assert _prefill(_cache(), _args(sm=sm)) == qsakv.ERR_BAD_SCALE
+        assert _decode(_cache(), _args(sm=sm)) == qsakv.ERR_BAD_SCALE
+    assert _prefill(_cache(), _args(R=0, sm=1e-30)) == qsakv.OK
     # unit scale passes validation (checked with a zero-row call: no launch)
     assert _prefill(_cache("e4m3", ks=1.0, vs=1.0), _args(R=0)) == qsakv.OK
     # int8 caches ignore k_scale / v_scale entirely
