@@ -15,8 +15,10 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Every pointer named "device" is device memory owned by the caller.  The
- *   library allocates nothing, keeps no mutable global state and is
- *   re-entrant.  Tensors are dense, row-major, with the shapes given below.
+ *   library allocates nothing and is re-entrant; its only mutable global
+ *   state is the static split-K scratch of qsa_sparse_attn_decode_noalloc
+ *   (one per GPU).  Tensors are dense, row-major, with the shapes given
+ *   below.
  * - `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *   enqueue work; none of them synchronizes.
  * - All shape, pointer, alignment, dtype and scale checks run on the host
@@ -64,7 +66,10 @@ typedef enum qkv_status {
                                misaligned                                   */
   QKV_ERR_HIP = 6,          /* the HIP runtime reported an error on launch;
                                qkv_last_hip_error() returns its code        */
-  QKV_ERR_ALIGNMENT = 7     /* a device pointer is not aligned as required  */
+  QKV_ERR_ALIGNMENT = 7,    /* a device pointer is not aligned as required  */
+  QKV_ERR_SCRATCH = 8       /* qsa_sparse_attn_decode_noalloc: the call needs
+                               more than QSA_NOALLOC_SCRATCH_BYTES of split-K
+                               scratch                                      */
 } qkv_status;
 
 typedef enum qkv_dtype {
@@ -232,6 +237,31 @@ QSAKV_API size_t qsa_decode_workspace_bytes(int32_t num_rows, int32_t num_q_head
 QSAKV_API qkv_status qsa_sparse_attn_decode(const qkv_cache *cache, const qsa_args *args,
                                   int32_t num_splits, void *workspace, size_t workspace_bytes,
                                   void *stream);
+
+/*
+ * qsa_sparse_attn_decode_noalloc -- qsa_sparse_attn_decode for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same computation, the same
+ * kernels and bitwise the same results, with the split-K partials in a
+ * static device buffer of QSA_NOALLOC_SCRATCH_BYTES that the library holds
+ * on each GPU it runs on until the process ends, instead of a caller
+ * workspace.  Calls no allocating routine.
+ *
+ *   num_splits  1..64; the call must fit the buffer:
+ *               qsa_decode_workspace_bytes(R, Hq, D, num_splits) <=
+ *               QSA_NOALLOC_SCRATCH_BYTES, else QKV_ERR_SCRATCH (checked on
+ *               the host, nothing launched).  num_splits = 1 uses no scratch.
+ * The buffer of a GPU is found (hipGetSymbolAddress) on the first call that
+ * runs there, on the stream's device.  Every call on one GPU shares that
+ * GPU's buffer and leaves its partials there: calls that overlap in time on
+ * one GPU (other streams, other threads) race and give undefined results;
+ * calls ordered on one stream are safe.  Other arguments and errors as
+ * qsa_sparse_attn_decode.
+ */
+#define QSA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+QSAKV_API qkv_status qsa_sparse_attn_decode_noalloc(const qkv_cache *cache, const qsa_args *args,
+                                                    int32_t num_splits, void *stream);
 
 /*
  * kv_calib_stats -- the per-tensor statistics that choose and audit an E4M3

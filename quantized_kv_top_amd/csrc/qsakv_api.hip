@@ -5,13 +5,49 @@
 #include <cstdint>
 #include <cstring>
 #include <limits>
+#include <mutex>
 
 #include "qsakv.h"
 #include "qsakv_internal.h"
 
+// Split-K scratch of qsa_sparse_attn_decode_noalloc.  Every GPU the library
+// runs on holds its own copy until the process ends.  In host code the name
+// is only a stand-in for the symbol: kernels and copies use the device
+// address that hipGetSymbolAddress returns for the current GPU.
+static __device__ __align__(256) unsigned char scratch[QSA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local int32_t g_last_hip_error = 0;
+
+// Device address of `scratch` on each GPU, looked up once per device (with
+// that device current) on the first no-alloc call that runs there.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_ptr(hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return e;
+    if (back != hipSuccess) return back;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 constexpr int64_t kI64Max = std::numeric_limits<int64_t>::max();
 
@@ -209,6 +245,36 @@ bool topk_ws(int64_t rows, int64_t stride, int64_t k, TopkWs* w) {
   return true;
 }
 
+// Checks shared by the two split-K entry points (nothing launched).
+qkv_status check_decode(const qkv_cache* cache, const qsa_args* args, int32_t num_splits) {
+  qkv_status st = check_cache(cache, true);
+  if (st != QKV_OK) return st;
+  st = check_args(cache, args);
+  if (st != QKV_OK) return st;
+  if (num_splits < 1 || num_splits > 64) return QKV_ERR_UNSUPPORTED;
+  int64_t items;
+  if (!mul_ok((int64_t)args->num_rows * cache->num_kv_heads, num_splits, &items) ||
+      items > INT32_MAX)
+    return QKV_ERR_BAD_SHAPE;
+  return QKV_OK;
+}
+
+// The split-K launches on a checked call: the partitions (into the
+// workspace `ws`, unused when num_splits == 1), then the merge.
+qkv_status run_decode(const qkv_cache* cache, const qsa_args* args, int32_t num_splits, char* ws,
+                      hipStream_t s) {
+  qsakv::AttnParams p = make_params(cache, args, num_splits);
+  if (num_splits == 1)
+    return finish(qsakv::launch_attn(cache->kind, cache->head_dim, p, s));
+  WsLayout l;
+  ws_layout(args->num_rows, args->num_q_heads, cache->head_dim, num_splits, &l);
+  p.ws_o = reinterpret_cast<float*>(ws);
+  p.ws_ml = reinterpret_cast<float*>(ws + l.o_bytes);
+  const hipError_t e = qsakv::launch_attn(cache->kind, cache->head_dim, p, s);
+  if (e != hipSuccess) return finish(e);
+  return finish(qsakv::launch_merge(cache->head_dim, p, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -262,31 +328,31 @@ size_t qsa_decode_workspace_bytes(int32_t num_rows, int32_t num_q_heads, int32_t
 
 qkv_status qsa_sparse_attn_decode(const qkv_cache* cache, const qsa_args* args, int32_t num_splits,
                                   void* workspace, size_t workspace_bytes, void* stream) {
-  qkv_status st = check_cache(cache, true);
-  if (st != QKV_OK) return st;
-  st = check_args(cache, args);
-  if (st != QKV_OK) return st;
-  if (num_splits < 1 || num_splits > 64) return QKV_ERR_UNSUPPORTED;
-  int64_t items;
-  if (!mul_ok((int64_t)args->num_rows * cache->num_kv_heads, num_splits, &items) ||
-      items > INT32_MAX)
-    return QKV_ERR_BAD_SHAPE;
-  if (args->num_rows == 0) return QKV_OK;
-  qsakv::AttnParams p = make_params(cache, args, num_splits);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (num_splits == 1)
-    return finish(qsakv::launch_attn(cache->kind, cache->head_dim, p, s));
-  const size_t need = ws_bytes(args->num_rows, args->num_q_heads, cache->head_dim, num_splits);
-  if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return QKV_ERR_WORKSPACE;
-  WsLayout l;
-  ws_layout(args->num_rows, args->num_q_heads, cache->head_dim, num_splits, &l);
-  char* ws = static_cast<char*>(workspace);
-  p.ws_o = reinterpret_cast<float*>(ws);
-  p.ws_ml = reinterpret_cast<float*>(ws + l.o_bytes);
-  const hipError_t e = qsakv::launch_attn(cache->kind, cache->head_dim, p, s);
-  if (e != hipSuccess) return finish(e);
-  return finish(qsakv::launch_merge(cache->head_dim, p, s));
+  const qkv_status st = check_decode(cache, args, num_splits);
+  if (st != QKV_OK || args->num_rows == 0) return st;
+  if (num_splits > 1) {
+    const size_t need = ws_bytes(args->num_rows, args->num_q_heads, cache->head_dim, num_splits);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+      return QKV_ERR_WORKSPACE;
+  }
+  return run_decode(cache, args, num_splits, static_cast<char*>(workspace),
+                    static_cast<hipStream_t>(stream));
 }
+
+qkv_status qsa_sparse_attn_decode_noalloc(const qkv_cache* cache, const qsa_args* args,
+                                          int32_t num_splits, void* stream) {
+  const qkv_status st = check_decode(cache, args, num_splits);
+  if (st != QKV_OK || args->num_rows == 0) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (num_splits == 1) return run_decode(cache, args, 1, nullptr, s);
+  const size_t need = ws_bytes(args->num_rows, args->num_q_heads, cache->head_dim, num_splits);
+  if (need > QSA_NOALLOC_SCRATCH_BYTES) return QKV_ERR_SCRATCH;
+  void* ws = nullptr;
+  const hipError_t e = scratch_ptr(s, &ws);
+  if (e != hipSuccess) return finish(e);
+  return run_decode(cache, args, num_splits, static_cast<char*>(ws), s);
+}
+
 
 size_t qkv_calib_workspace_bytes(void) { return qsakv::calib_workspace_bytes(); }
 
@@ -381,6 +447,10 @@ const char* qkv_status_str(int32_t status) {
     case QKV_ERR_WORKSPACE: return "QKV_ERR_WORKSPACE: split-K workspace missing, small or misaligned";
     case QKV_ERR_HIP: return "QKV_ERR_HIP: the HIP runtime reported an error";
     case QKV_ERR_ALIGNMENT: return "QKV_ERR_ALIGNMENT: device pointer misaligned";
+    case QKV_ERR_SCRATCH:
+      return "QKV_ERR_SCRATCH: the call needs more split-K scratch than the no-alloc entry "
+             "point's static buffer holds (QSA_NOALLOC_SCRATCH_BYTES); use "
+             "qsa_sparse_attn_decode with a workspace";
     default: return "unknown qkv_status";
   }
 }

@@ -15,7 +15,9 @@ LIB_PATH = os.path.join(_PKG, "libqsakv.so")
 
 # status codes (qkv_status)
 OK, ERR_NULL, ERR_BAD_SHAPE, ERR_UNSUPPORTED, ERR_BAD_SCALE, ERR_WORKSPACE, ERR_HIP, \
-    ERR_ALIGNMENT = range(8)
+    ERR_ALIGNMENT, ERR_SCRATCH = range(9)
+# QSA_NOALLOC_SCRATCH_BYTES: split-K scratch of qsa_sparse_attn_decode_noalloc
+NOALLOC_SCRATCH_BYTES = 16 << 20
 # dtypes (qkv_dtype)
 BF16, FP16, FP32 = 0, 1, 2
 # cache kinds (qkv_cache_kind)
@@ -24,7 +26,8 @@ KIND_BY_NAME = {"int8": CACHE_INT8, "int8_inline": CACHE_INT8_INLINE,
                 "e4m3": CACHE_E4M3, "bf16": CACHE_BF16, "nvfp4": CACHE_NVFP4}
 
 EXPORTED = ("kv_quant_write", "qsa_sparse_attn_prefill", "qsa_decode_workspace_bytes",
-            "qsa_sparse_attn_decode", "qkv_calib_workspace_bytes", "kv_calib_stats",
+            "qsa_sparse_attn_decode", "qsa_sparse_attn_decode_noalloc",
+            "qkv_calib_workspace_bytes", "kv_calib_stats",
             "qsa_topk_workspace_bytes", "qsa_topk_select", "qkv_cache_bytes",
             "qkv_status_str", "qkv_last_hip_error", "qkv_abi_version")
 
@@ -78,6 +81,8 @@ def lib():
     L.qsa_decode_workspace_bytes.restype = c_sz
     L.qsa_sparse_attn_decode.argtypes = [P(QkvCache), P(QsaArgs), c_i32, c_vp, c_sz, c_vp]
     L.qsa_sparse_attn_decode.restype = c_i32
+    L.qsa_sparse_attn_decode_noalloc.argtypes = [P(QkvCache), P(QsaArgs), c_i32, c_vp]
+    L.qsa_sparse_attn_decode_noalloc.restype = c_i32
     L.qkv_calib_workspace_bytes.argtypes = []
     L.qkv_calib_workspace_bytes.restype = c_sz
     L.kv_calib_stats.argtypes = [c_vp, c_i32, c_i64, ctypes.c_float, c_vp, c_vp, c_sz, c_vp]
@@ -274,6 +279,21 @@ def qsa_sparse_attn_decode(cache, q, row_seq, block_table, topk_idx, sm_scale, o
     wb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().qsa_sparse_attn_decode(ctypes.byref(d), ctypes.byref(a), num_splits, wp, wb,
                                         _stream(stream)), "qsa_sparse_attn_decode")
+
+
+def qsa_sparse_attn_decode_noalloc(cache, q, row_seq, block_table, topk_idx, sm_scale, out,
+                                   num_splits, lse=None, stream=None):
+    """Split-K sparse attention with the partials in the library's static
+    per-GPU scratch (no workspace argument, nothing allocated); calls that
+    overlap in time on one GPU race."""
+    _check_attn(q, row_seq, block_table, topk_idx, out, lse)
+    _on_device(q=q, out=out, row_seq=row_seq, block_table=block_table, topk_idx=topk_idx,
+               lse=lse)
+    a = _qsa_args(q, row_seq, block_table, topk_idx, sm_scale, out, lse)
+    d = cache.desc()
+    _check(lib().qsa_sparse_attn_decode_noalloc(ctypes.byref(d), ctypes.byref(a), num_splits,
+                                                _stream(stream)),
+           "qsa_sparse_attn_decode_noalloc")
 
 
 def calib_workspace_bytes():

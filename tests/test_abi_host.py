@@ -243,3 +243,30 @@ def test_topk_workspace_bytes():
     assert L.qsa_topk_workspace_bytes(4, 1 << 20, 2048) == 0
     # k too large for segments: streamed, no workspace
     assert L.qsa_topk_workspace_bytes(4, 1 << 20, 8192) == 0
+
+
+def _decode_noalloc(c, a, P=8):
+    return qsakv.lib().qsa_sparse_attn_decode_noalloc(ctypes.byref(c), ctypes.byref(a), P, None)
+
+
+def test_noalloc_decode_host_checks():
+    """The no-alloc decode validates like qsa_sparse_attn_decode and refuses,
+    before any HIP call, a call whose split-K partials exceed its static
+    scratch (QSA_NOALLOC_SCRATCH_BYTES)."""
+    L = qsakv.lib()
+    assert qsakv.NOALLOC_SCRATCH_BYTES == 16 << 20
+    # 127 rows x 16 heads x 8 splits at D = 256 fit; 128 rows do not
+    assert L.qsa_decode_workspace_bytes(127, 16, 256, 8) <= qsakv.NOALLOC_SCRATCH_BYTES
+    assert L.qsa_decode_workspace_bytes(128, 16, 256, 8) > qsakv.NOALLOC_SCRATCH_BYTES
+    big = _cache(D=256, H=2)
+    assert _decode_noalloc(big, _args(R=128, Hq=16)) == qsakv.ERR_SCRATCH
+    assert _decode_noalloc(big, _args(R=4000, Hq=16), P=64) == qsakv.ERR_SCRATCH
+    assert "QSA_NOALLOC_SCRATCH_BYTES" in L.qkv_status_str(qsakv.ERR_SCRATCH).decode()
+    # the same argument checks as the workspace variant
+    assert _decode_noalloc(_cache(), _args(sm=0.0)) == qsakv.ERR_BAD_SCALE
+    assert _decode_noalloc(_cache(), _args(), P=0) == qsakv.ERR_UNSUPPORTED
+    assert _decode_noalloc(_cache(), _args(), P=65) == qsakv.ERR_UNSUPPORTED
+    assert _decode_noalloc(_cache(D=64), _args()) == qsakv.ERR_UNSUPPORTED
+    assert _decode_noalloc(_cache(), _args(q=DUMMY + 4)) == qsakv.ERR_ALIGNMENT
+    assert _decode_noalloc(_cache("e4m3", ks=0.0), _args()) == qsakv.ERR_BAD_SCALE
+    assert _decode_noalloc(_cache(), _args(R=0)) == qsakv.OK
