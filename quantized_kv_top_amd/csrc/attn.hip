@@ -789,12 +789,12 @@ void qsa_attn16_kernel(AttnParams p) {
 // Log-sum-exp merge of the split-K partials of one (row, head) per wave:
 // M = max_p m_p, L = sum_p L_p 2^(m_p - M), out = sum_p o_p 2^(m_p - M) / L,
 // times the E4M3 V scale (applied once, after the merge).  Each lane owns
-// D/64 outputs; the first partials are loaded together with the (max, sum)
-// pairs, so the call costs about one memory round trip.
-template <int D>
+// D/64 outputs; the first kPre partials (every one, for P <= kPre: the host
+// picks kPre = 8 or 16 by P) are loaded together with the (max, sum) pairs,
+// so the call costs about one memory round trip.
+template <int D, int kPre>
 __global__ __launch_bounds__(kWave) void qsa_merge_kernel(AttnParams p) {
   constexpr int E = D / kWave;
-  constexpr int kPre = 8;
   const int lane = lane_id();
   // (row, query head) r * Hq + h; consecutive ones share an XCD, in the same
   // split as the attention launch's items, so that a head's partials are
@@ -809,34 +809,35 @@ __global__ __launch_bounds__(kWave) void qsa_merge_kernel(AttnParams p) {
   const int P = p.num_splits;
   const int64_t base = rh * P;
   const float* src = p.ws_o + base * D + lane * E;
+  // every load is issued, with no branch between them (a conditional load
+  // makes the compiler copy its register and wait for it): slots past P
+  // re-read the last partial and get weight 0 below (P >= 2 here)
   float pre[kPre][E];
 #pragma unroll
   for (int q = 0; q < kPre; ++q) {
-    if (q < P) {
-      if constexpr (E == 4) {
-        const float4 v = *reinterpret_cast<const float4*>(src + (int64_t)q * D);
-        pre[q][0] = v.x; pre[q][1] = v.y; pre[q][2] = v.z; pre[q][3] = v.w;
-      } else {
-        const float2 v = *reinterpret_cast<const float2*>(src + (int64_t)q * D);
-        pre[q][0] = v.x; pre[q][1] = v.y;
-      }
+    const int64_t qq = q < P ? q : P - 1;
+    if constexpr (E == 4) {
+      const float4 v = *reinterpret_cast<const float4*>(src + qq * D);
+      pre[q][0] = v.x; pre[q][1] = v.y; pre[q][2] = v.z; pre[q][3] = v.w;
     } else {
-#pragma unroll
-      for (int i = 0; i < E; ++i) pre[q][i] = 0.f;
+      const float2 v = *reinterpret_cast<const float2*>(src + qq * D);
+      pre[q][0] = v.x; pre[q][1] = v.y;
     }
   }
-  // the partitions' (max, sum) pairs sit at workgroup-uniform addresses:
-  // every lane reads them (scalar loads) -- no cross-lane reductions
+  // the partitions' (max, sum) pairs: lane q loads pair q with the partials
+  // (one vector load, the same round trip), then every lane reads them
+  // across lanes -- no reductions, and no scalar loads (more than 15 of
+  // those in flight would be split into two round trips)
   const float* ml = p.ws_ml + 2 * base;
+  const int lq_idx = (lane & (kPre - 1)) < P ? (lane & (kPre - 1)) : P - 1;
+  const float2 mlv = *reinterpret_cast<const float2*>(ml + 2 * lq_idx);
   float mq[kPre], lq[kPre];
 #pragma unroll
   for (int q = 0; q < kPre; ++q) {
-    mq[q] = kNegInf;
-    lq[q] = 0.f;
-    if (q < P) {                                            // uniform
-      mq[q] = ml[2 * q];
-      lq[q] = ml[2 * q + 1];
-    }
+    const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mlv.x), q));
+    const float l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mlv.y), q));
+    mq[q] = q < P ? m : kNegInf;
+    lq[q] = q < P ? l : 0.f;
   }
   float M = kNegInf;
 #pragma unroll
@@ -923,12 +924,20 @@ hipError_t launch_attn(int kind, int head_dim, const AttnParams& p, hipStream_t 
   }
 }
 
+template <int D>
+void launch_merge_d(const AttnParams& p, unsigned grid, hipStream_t s) {
+  if (p.num_splits <= 8)
+    qsa_merge_kernel<D, 8><<<grid, dim3(kWave), 0, s>>>(p);
+  else
+    qsa_merge_kernel<D, 16><<<grid, dim3(kWave), 0, s>>>(p);
+}
+
 hipError_t launch_merge(int head_dim, const AttnParams& p, hipStream_t s) {
   const unsigned grid = (unsigned)(p.num_rows * p.num_q_heads);
   if (head_dim == 256)
-    qsa_merge_kernel<256><<<grid, dim3(kWave), 0, s>>>(p);
+    launch_merge_d<256>(p, grid, s);
   else
-    qsa_merge_kernel<128><<<grid, dim3(kWave), 0, s>>>(p);
+    launch_merge_d<128>(p, grid, s);
   return hipGetLastError();
 }
 
