@@ -23,8 +23,9 @@ The shapes and distributions follow the workloads the pages measure
             N(0,1); 5 query rows per seq (1 + 4 speculative) at ctx-5..ctx-1;
             top-k 2048 = 1434 distinct from the last 4096 positions + 614
             distinct from before them, sorted; 8 split-K partitions.
-* e4m3      12 layers, 4 seqs x ctx 65536, Hq 32 / Hkv 4, D 128, BS 64,
-            K/V fp16(0.5 * t_4) (Student-t, nu = 4); 1 row per seq at 65535;
+* e4m3      12 layers, 4 seqs x ctx 65536, Hq 32 / Hkv 4, D 128, BS 64
+            (one block table for all layers), K/V fp16(0.5 * t_4)
+            (Student-t, nu = 4); 1 row per seq at 65535;
             top-k 2051 distinct uniform causal; fp16 Q/out (top-k 2051 as on
             page "[Perf][SM70][FP8] Hoist QSA E4M3 KV scales", section "Test
             plan").
@@ -213,12 +214,19 @@ def prefill(device="cpu", seed=2, num_rows=2048, topk=1024, ctx=32768, pool_bloc
 
 
 def decode(device="cpu", seed=3, num_seqs=8, ctx=131072, rows_per_seq=5, topk=2048,
-           pool_blocks=None, num_splits=8):
+           pool_blocks=None, num_splits=8, layer=None):
+    """The decode workload; ``layer`` = i draws layer i of a model over the
+    same sequences: the block table is the model's (drawn from ``seed``
+    alone, shared by every layer, as one paged cache serves all layers),
+    the lists, queries and K/V are the layer's own."""
     rng = np.random.default_rng(seed)
     Hq, Hkv, D, BS = 16, 2, 256, 64
     nb = ctx // BS
     pool_blocks = pool_blocks or (num_seqs * nb + num_seqs * nb // 8)
     bt = scattered_block_table(rng, num_seqs, nb, pool_blocks)
+    if layer is not None:
+        rng = np.random.default_rng([seed, layer])
+        seed = seed * 100 + layer
     row_seq, idx, positions = [], [], []
     for b in range(num_seqs):
         for p in range(ctx - rows_per_seq, ctx):
@@ -240,12 +248,14 @@ def decode(device="cpu", seed=3, num_seqs=8, ctx=131072, rows_per_seq=5, topk=20
 
 def e4m3_layer(layer, device="cpu", seed=4, num_seqs=4, ctx=65536, topk=2051,
                pool_blocks=None, num_splits=8):
-    """Layer ``layer`` (0..11) of the E4M3 workload; K/V are fp16 sources."""
-    rng = np.random.default_rng([seed, layer])
+    """Layer ``layer`` (0..11) of the E4M3 workload; K/V are fp16 sources.
+    The block table is the model's (drawn from ``seed`` alone: every layer
+    pages the same sequences the same way); lists and data are per layer."""
     Hq, Hkv, D, BS = 32, 4, 128, 64
     nb = ctx // BS
     pool_blocks = pool_blocks or num_seqs * nb
-    bt = scattered_block_table(rng, num_seqs, nb, pool_blocks)
+    bt = scattered_block_table(np.random.default_rng(seed), num_seqs, nb, pool_blocks)
+    rng = np.random.default_rng([seed, layer])
     row_seq = np.arange(num_seqs, dtype=np.int32)
     idx = np.stack([draw_sorted_distinct(rng, topk, 0, ctx - 1) for _ in range(num_seqs)])
     T = num_seqs * ctx
