@@ -31,13 +31,12 @@
 //
 // Exact operands.  E4M3 codes become fp16 through gfx950's OCP-FP8 convert.
 // An int8 code q becomes the fp16 value 1152 + q (0x64 in the high byte and
-// q + 128 in the low byte -- exact, one byte permute per pair).  K operands
-// then have the 1152 subtracted in fp16 (exact), so the logits accumulate
-// the products q * Q alone.  V operands keep it: it is removed from the
-// output after the MFMA as 1152 * sum_t W_t (the sum of exactly the weights
-// that entered the MFMA); in value units the offset is 1152 * s_v ~ 9
-// max|v|, so its share of the fp32 accumulation error stays ~2^-21 max|v|
-// per accumulation step.  Queries are rounded to fp16 after an exact
+// q + 128 in the low byte -- exact, one byte permute per pair), then q itself
+// by a packed fp16 subtract of 1152 (exact).  With the offset left in, the
+// fp32 accumulators would carry 1152 * sum(Q) (logits) and 1152 * sum(W)
+// (outputs) -- terms that can dwarf the signal (outlier keys with
+// nonzero-mean queries; concentrated weights over small outputs) and whose
+// rounding would land on it.  Queries are rounded to fp16 after an exact
 // power-of-two prescale; bf16 caches run bf16 MFMA directly (their query
 // operand staged in LDS at D = 256, where the registers go to the tiles in
 // flight).
@@ -62,7 +61,6 @@ constexpr int pos_per_thread() { return 1024 / (NW * 64) < 4 ? 1024 / (NW * 64) 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kMaxSlack = 8.f;      // log2 units the running max may lag behind
 constexpr float kSigSlack = 16.f;     // factor sigma may lag behind a tile's V scale
-constexpr float kI8Bias = 1152.f;     // fp16(0x64XX) = 1024 + XX, XX = q + 128
 
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -200,7 +198,6 @@ struct WaveState {
   float l;     // this lane's partial sum of exp2(logit - m)
   float sig;   // reference V scale (int8 kinds), wave-uniform
   float rsig;  // 1 / sig (0 while sig is 0)
-  float cw;    // this lane's partial sum of the PV weights (int8 bias removal)
 };
 
 template <int KIND>
@@ -238,7 +235,7 @@ __device__ __forceinline__ uint32_t v_pair_f16(const uint32_t (&tk)[2], int bb) 
   if constexpr (KIND == kE4M3)
     return hi ? e4m3pair_to_f16x2<true>(tk[half]) : e4m3pair_to_f16x2<false>(tk[half]);
   else
-    return i8pair_to_f16x2(tk[half], hi ? kSelB23 : kSelB01);
+    return i8pair_unbias(i8pair_to_f16x2(tk[half], hi ? kSelB23 : kSelB01));
 }
 
 template <int KIND, int D, int TT, typename QS>
@@ -334,18 +331,13 @@ __device__ __forceinline__ void compute_tile(const TileRaw<KIND, D, TT>& t, cons
       st.rsig = 1.f / smax;
     }
     const float rs = st.rsig;
-    float wsum = 0.f;
 #pragma unroll
     for (int e = 0; e < NT; ++e) {
-      // the weight as it enters the MFMA (fp16), so that the bias removed
-      // afterwards is exactly the one the MFMA added.  A padding token reads
-      // row 0's scale: it is replaced by 0 (a NaN or inf stored there would
-      // otherwise turn the zero weight into NaN).
+      // A padding token reads row 0's scale: it is replaced by 0 (a NaN or
+      // inf stored there would otherwise turn the zero weight into NaN).
       const float sv = ((t.valid >> e) & 1u) ? t.sv[e] : 0.f;
-      w[e] = (float)(_Float16)(pr[e] * (sv * rs));
-      wsum += w[e];
+      w[e] = pr[e] * (sv * rs);
     }
-    st.cw = st.cw * beta + wsum;
   } else {
 #pragma unroll
     for (int e = 0; e < NT; ++e) w[e] = pr[e];
@@ -633,7 +625,7 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
   }
 
   // ---- the wave's tiles -----------------------------------------------------
-  WaveState st{kNegInf, 0.f, 0.f, 0.f, 0.f};
+  WaveState st{kNegInf, 0.f, 0.f, 0.f};
   f32x4 o[G::kPV];
 #pragma unroll
   for (int j = 0; j < G::kPV; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -689,11 +681,6 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
   // wave 0's buffer -- two barriers in all, a fixed order (bitwise
   // reproducible); the total ends in wave 0.
   const float l_h = group4_sum(st.l);
-  if constexpr (G::kInt) {
-    const float corr = kI8Bias * group4_sum(st.cw);
-#pragma unroll
-    for (int j = 0; j < G::kPV; ++j) o[j] -= corr;
-  }
   if (grp == 0) {
     s_m[w][ln16] = st.m;
     s_l[w][ln16] = l_h;
