@@ -163,6 +163,58 @@ def test_e4m3_encoder_bit_sweep(scale):
     assert np.all(got[nan] & 0x7F == 0x7F)
 
 
+def test_e4m3_encoder_exhaustive():
+    """Every fp32 bit pattern -- 2^32 values: both signs, every exponent and
+    mantissa, subnormals, +-inf and every NaN payload -- written through
+    kv_quant_write into an E4M3 cache at scale 1.0, each code equal to the
+    oracle's encoding of the same pattern (the converter contract
+    stored = e4m3fn(x / scale) of page "Qwen3.8 Flash Next NVFP4 QSA FP8 E4M3
+    KV Scales", section "Calibration"; NaN sources keep their sign).  Each
+    call writes 2^28 patterns as K rows and the next 2^28 as V rows; the
+    oracle side runs in chunks on a pool of host threads."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    D, H, BS = 256, 1, 64
+    half = 1 << 28
+    T = half // D
+    c = qsakv.Cache("e4m3", T // BS, BS, H, D, k_scale=1.0, v_scale=1.0, zero=False)
+    slots = torch.arange(T, dtype=torch.int64, device="cuda")
+    CH = 1 << 22
+    nthreads = max(1, min(16, int(os.environ.get("OMP_NUM_THREADS", 0)) or (os.cpu_count() or 1)))
+
+    def patterns(start):             # int32 tensor of the bit patterns start .. start + half
+        lo = start - (1 << 32) if start >= (1 << 31) else start
+        return torch.arange(lo, lo + half, dtype=torch.int32, device="cuda")
+
+    def check(got, start, off):
+        with np.errstate(all="ignore"):
+            x = np.arange(start + off, start + off + CH, dtype=np.uint64).astype(np.uint32)
+            want = ofmt.e4m3_quantize(x.view(np.float32), np.float32(1.0))
+        bad = np.flatnonzero(got[off:off + CH] != want)
+        return int(bad.size), [hex(start + off + int(b)) for b in bad[:4]]
+
+    total = 0
+    with ThreadPoolExecutor(nthreads) as pool:
+        for base in range(0, 1 << 32, 2 * half):
+            k = patterns(base).view(torch.float32).reshape(T, H, D)
+            v = patterns(base + half).view(torch.float32).reshape(T, H, D)
+            qsakv.kv_quant_write(c, k, v, slots)
+            got_k = c.k.cpu().numpy()
+            got_v = c.v.cpu().numpy()
+            del k, v
+            futs = [pool.submit(check, got, start, off)
+                    for got, start in ((got_k, base), (got_v, base + half))
+                    for off in range(0, half, CH)]
+            res = [f.result() for f in futs]
+            bad = sum(r[0] for r in res)
+            first = [h for r in res for h in r[1]][:4]
+            total += 2 * half
+            say("e4m3 exhaustive: patterns 0x%08x..0x%08x checked (%d threads), mismatches %d %s"
+                % (base, base + 2 * half - 1, nthreads, bad, first))
+            assert bad == 0, "codes differ from the oracle at fp32 patterns %s" % first
+    assert total == 1 << 32
+
+
 @pytest.mark.parametrize("g", [1.0, 0.0021, 3.0e-6])
 def test_nvfp4_blocks_sweep(g):
     """NVFP4 rows whose blocks hold the fp32 sweep values (NaN, +-inf,
