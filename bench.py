@@ -389,6 +389,7 @@ def bench_decode(args):
     L = args.layers or 8
     kind = args.kind or "int8"
     ms_call, rows, b = run_decode(kind, L, args.splits, args.steps, args.warmup)
+    cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_rows(lambda: [wl.decode(device="cpu", seed=200, layer=0)], kind,
                                 args.cpu_budget, "all 40 decode rows of one layer, top-k 2048")

@@ -60,3 +60,27 @@ def test_source_sha_covers_the_attention_sources():
     a = bench.source_sha()
     assert len(a) == 16 and a == bench.source_sha()
     assert "attn.hip" in bench.ATTN_SOURCES
+
+
+def test_bench_lines_use_only_assigned_names():
+    """Every name a bench_* function returns is assigned on every path
+    (at its top level, or in a with-block, which always runs) -- a config's
+    JSON line must not depend on a branch such as the CPU-baseline one."""
+    import ast
+    tree = ast.parse(open(os.path.join(ROOT, "bench.py")).read())
+    bad = []
+    for fn in (n for n in tree.body if isinstance(n, ast.FunctionDef) and n.name.startswith("bench_")):
+        sure, maybe = {a.arg for a in fn.args.args}, set()
+        for st in fn.body:
+            blocks = st.body if isinstance(st, ast.With) else [st]
+            for b in blocks:
+                target = maybe if isinstance(b, (ast.If, ast.For, ast.While, ast.Try)) else sure
+                for n in ast.walk(b):
+                    if isinstance(n, ast.Name) and isinstance(n.ctx, ast.Store):
+                        target.add(n.id)
+        for st in fn.body:
+            if isinstance(st, ast.Return) and st.value is not None:
+                for n in ast.walk(st.value):
+                    if isinstance(n, ast.Name) and n.id in maybe and n.id not in sure:
+                        bad.append((fn.name, n.id))
+    assert not bad, bad
