@@ -8,7 +8,8 @@ so that more than twice the 256 MB last-level cache passes between two
 visits of the same cache.  Prints ONE JSON line, whose "sub" object also
 times the tiny workload, the decode workload (split-K 8), the 12-layer E4M3
 step (split-K 16) and the end-to-end chunk prefills in their 13.75 GiB pools
-(HBM-resident), each against the 8 TB/s HBM peak (--no-sub skips them).
+(whose gathers miss the L2), each against the 8 TB/s HBM peak (--no-sub
+skips them).
 
 Other workloads (``--config``) print their own line for the record:
 decode (8 x 128K, 40 rows, top-k 2048, split-K 8), e4m3 (12 layers, 4 rows,
@@ -277,8 +278,10 @@ def bench_prefill(args):
                      "frac_step_span": bytes_launch / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
                      "cache_resident": "last-level cache: each 34 MB layer cache is re-read "
                                        "~64x within one launch, so most gathers are served "
-                                       "by the 256 MB MALL; the HBM-resident rates are the "
-                                       "e2e_chunk_prefill sub-records",
+                                       "by the 256 MB MALL; the e2e_chunk_prefill "
+                                       "sub-records gather from 13.75 GiB pools whose reads "
+                                       "miss the L2 (L2-to-fabric traffic 0.98-1.08x the "
+                                       "gathered bytes)",
                      "traffic_over_algorithmic": None if traffic is None
                      else traffic / bytes_launch},
     }
@@ -871,8 +874,8 @@ def sub_e2e_prefill(args, kinds=("int8", "e4m3", "bf16")):
         b = R * gathered_bytes_per_row(kind, topk, 2, 256)
         recs[kind] = sub_record(
             "e2e chunk prefill: 8192 rows x top-k 1024 over one 131K-token sequence whose "
-            "blocks are spread over a 13.75 GiB %s pool (HBM-resident), Hq 16 / Hkv 2, D 256; "
-            "2 layers rotated" % kind, total / args.steps, R, b,
+            "blocks are spread over a 13.75 GiB %s pool (gathers miss the L2), Hq 16 / Hkv 2, "
+            "D 256; 2 layers rotated" % kind, total / args.steps, R, b,
             "hipEvents around the steps", pool_tokens=int(layers[0].pool_blocks) * 64)
         del layers, e
         torch.cuda.synchronize()
