@@ -840,12 +840,21 @@ def sub_tiny(args):
     return rec
 
 
+# oracle seconds per sub-record baseline (the main line's takes --cpu-budget)
+SUB_CPU_BUDGET = 8.0
+
+
 def sub_decode(args):
     ms, rows, b = run_decode("int8", 8, 8, args.steps, args.warmup)
-    return sub_record("decode: 8 seqs x 128K ctx, 40 rows (5 per seq), top-k 2048 (70% "
-                      "recent window), Hq 16 / Hkv 2, D 256, int8, split-K 8 + merge; 8 layers "
-                      "(one block table) rotated", ms, rows, b,
-                      "graph of the 8 layers' calls, per call", num_splits=8)
+    rec = sub_record("decode: 8 seqs x 128K ctx, 40 rows (5 per seq), top-k 2048 (70% "
+                     "recent window), Hq 16 / Hkv 2, D 256, int8, split-K 8 + merge; 8 layers "
+                     "(one block table) rotated", ms, rows, b,
+                     "graph of the 8 layers' calls, per call", num_splits=8)
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_rows(
+            lambda: [wl.decode(device="cpu", seed=200, layer=0)], "int8",
+            min(args.cpu_budget, SUB_CPU_BUDGET), "all 40 decode rows of one layer, top-k 2048")
+    return rec
 
 
 C4_SPLITS = 16
@@ -853,11 +862,29 @@ C4_SPLITS = 16
 
 def sub_e4m3(args):
     ms, rows, b = run_e4m3("e4m3", 4, C4_SPLITS, args.steps, args.warmup)
-    return sub_record("e4m3: 12 layers x 4 rows, top-k 2051, Hq 32 / Hkv 4, D 128, calibrated "
-                      "E4M3 caches, split-K %d + merge; 4 independent 12-layer models rotated; "
-                      "per 12-layer step" % C4_SPLITS, ms, 12 * rows, b,
-                      "graph of 4 x 12 layer calls, per 12-layer step",
-                      num_splits=C4_SPLITS, unit_rows="layer-rows")
+    rec = sub_record("e4m3: 12 layers x 4 rows, top-k 2051, Hq 32 / Hkv 4, D 128, calibrated "
+                     "E4M3 caches, split-K %d + merge; 4 independent 12-layer models rotated; "
+                     "per 12-layer step" % C4_SPLITS, ms, 12 * rows, b,
+                     "graph of 4 x 12 layer calls, per 12-layer step",
+                     num_splits=C4_SPLITS, unit_rows="layer-rows")
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_rows(
+            lambda: [wl.e4m3_layer(i, device="cpu", seed=4) for i in range(3)], "e4m3",
+            min(args.cpu_budget, SUB_CPU_BUDGET), "the 4 rows of layers 0-2 of 12 (layer-rows)")
+    return rec
+
+
+def e2e_chunk_oracle_workload(rows=512):
+    """The first ``rows`` rows of the end-to-end chunk prefill for the oracle:
+    the sequence's 131,072 existing and chunk tokens in a cache of exactly
+    its 2049 blocks (where the blocks sit in a pool does not change the
+    oracle's arithmetic, only the size of the host arrays)."""
+    e = wl.e2e(2049, device="cpu", seed=5)
+    return wl.Workload("e2e chunk", e.num_q_heads, e.num_kv_heads, e.head_dim, e.block_size,
+                       2049, "bf16", "bf16", "bf16", torch.cat([e.ctx_k, e.chunk_k]),
+                       torch.cat([e.ctx_v, e.chunk_v]),
+                       np.concatenate([e.ctx_slots, e.chunk_slots]), e.chunk_q[:rows],
+                       np.zeros(rows, np.int32), e.block_table, e.chunk_topk[:rows], e.sm_scale)
 
 
 def sub_e2e_prefill(args, kinds=("int8", "e4m3", "bf16")):
@@ -877,6 +904,11 @@ def sub_e2e_prefill(args, kinds=("int8", "e4m3", "bf16")):
             "blocks are spread over a 13.75 GiB %s pool (gathers miss the L2), Hq 16 / Hkv 2, "
             "D 256; 2 layers rotated" % kind, total / args.steps, R, b,
             "hipEvents around the steps", pool_tokens=int(layers[0].pool_blocks) * 64)
+        if kind == "int8" and not args.no_cpu_baseline:
+            recs[kind]["cpu_baseline"] = cpu_baseline_rows(
+                lambda: [e2e_chunk_oracle_workload()], "int8",
+                min(args.cpu_budget, SUB_CPU_BUDGET),
+                "the first 512 of the 8192 chunk rows, top-k 1024")
         del layers, e
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
