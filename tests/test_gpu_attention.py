@@ -564,7 +564,7 @@ def _random_case(seed):
     return kind, w, P, od
 
 
-@pytest.mark.parametrize("seed", list(range(100, 124)))
+@pytest.mark.parametrize("seed", list(range(100, 260)))
 def test_random_configurations(seed):
     kind, w, P, od = _random_case(seed)
     say("random", seed, kind, "D", w.head_dim, "BS", w.block_size, "G",
