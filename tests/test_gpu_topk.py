@@ -156,3 +156,38 @@ def test_lists_drive_the_attention():
         n = min(int(s.row_len[r]), s.topk)
         assert (np.diff(g[r, :n]) > 0).all() and g[r, 0] >= 0 and g[r, n - 1] < s.row_len[r]
         assert (g[r, n:] == -1).all()
+
+
+def _random_topk_case(seed):
+    """A seeded random selection: dtype, rows, row stride (a multiple of 8
+    up to 160K, so that long rows take the segmented path), k, row lengths
+    (including 0, <= k, the stride and clamped values beyond it) and a score
+    distribution (normal, a few distinct values, or normal with NaN / +-inf
+    sprinkled in)."""
+    rng = np.random.default_rng(seed)
+    dtype = DTYPES[rng.integers(len(DTYPES))]
+    R = int(rng.integers(1, 9))
+    stride = int(rng.choice([8, 64, 1000, 4096, 32768, 40000, 70000, 131072, 163840]))
+    stride = -(-stride // 8) * 8
+    k = int(rng.integers(1, min(stride, 4096) + 1))
+    lens = rng.integers(0, stride + 1, size=R).astype(np.int64)
+    picks = [0, 1, k, k + 1, stride, stride + 100]
+    for i in range(min(R, 2)):
+        lens[i] = picks[rng.integers(len(picks))]
+    mode = int(rng.integers(3))
+    v = rng.standard_normal((R, stride)).astype(np.float32)
+    if mode == 1:
+        pool = np.array([0.0, -0.0, 1.0, -1.0, 0.25, 3.0], np.float32)
+        v = pool[rng.integers(0, pool.size, size=(R, stride))]
+    elif mode == 2:
+        m = rng.random((R, stride))
+        v[m < 0.01] = np.nan
+        v[(m >= 0.01) & (m < 0.015)] = np.inf
+        v[(m >= 0.015) & (m < 0.02)] = -np.inf
+    return torch.from_numpy(v).to(dtype).cuda(), lens.astype(np.int32), k, mode
+
+
+@pytest.mark.parametrize("seed", list(range(300, 360)))
+def test_random_selections(seed):
+    x, lens, k, mode = _random_topk_case(seed)
+    _check(x, lens, k, "random seed %d mode %d" % (seed, mode))
