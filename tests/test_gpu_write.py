@@ -262,3 +262,43 @@ def test_write_is_deterministic_and_launch_independent():
     qsakv.kv_quant_write(c, ks[1000:].contiguous(), vs[1000:].contiguous(), sm[1000:])
     torch.cuda.synchronize()
     assert torch.equal(a.k, c.k) and torch.equal(a.kv_scale, c.kv_scale)
+
+
+@pytest.mark.parametrize("seed", list(range(500, 540)))
+def test_random_writes(seed):
+    """A seeded random write: cache kind, D, Hkv, block size, pool size,
+    token count, source dtype, magnitudes over many octaves, layer scales,
+    and slots with skipped (-1) and out-of-range entries; every slot's bytes
+    against the oracle."""
+    rng = np.random.default_rng(seed)
+    kind = KINDS[rng.integers(len(KINDS))]
+    D = int(rng.choice([128, 256]))
+    H = int(rng.integers(1, 5))
+    BS = int(2 ** rng.integers(0, 8))
+    NB = int(rng.integers(1, 2048 // BS + 2))
+    T = int(rng.integers(1, NB * BS + 1))
+    src = str(rng.choice(["fp32", "bf16", "fp16"]))
+    x = (rng.standard_normal((T, H, D)) *
+         np.exp2(rng.uniform(-10, 6, (T, H, 1)))).astype(np.float32)
+    y = (rng.standard_normal((T, H, D)) *
+         np.exp2(rng.uniform(-10, 6, (T, H, 1)))).astype(np.float32)
+    tdt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[src]
+    slots = rng.permutation(NB * BS)[:T].astype(np.int64)
+    drop = rng.random(T)
+    slots[drop < 0.05] = -1
+    slots[(drop >= 0.05) & (drop < 0.07)] = NB * BS + 5
+    w = wl.Workload("t", H, H, D, BS, NB, "bf16", "fp32", src, torch.from_numpy(x).to(tdt),
+                    torch.from_numpy(y).to(tdt), slots,
+                    torch.zeros(1, H, D, dtype=torch.bfloat16), np.zeros(1, np.int32),
+                    np.zeros((1, 1), np.int32), np.zeros((1, 1), np.int32), 0.1)
+    ks = vs = None
+    if kind == "e4m3":
+        ks, vs = float(np.exp2(rng.uniform(-8, 2))), float(np.exp2(rng.uniform(-8, 2)))
+    elif kind == "nvfp4":
+        ks, vs = float(np.exp2(rng.uniform(-14, -2))), float(np.exp2(rng.uniform(-14, -2)))
+    say("random write", seed, kind, "D", D, "H", H, "BS", BS, "NB", NB, "T", T, src)
+    c = gpu_write(kind, w, ks or 1.0, vs or 1.0)
+    good = (slots >= 0) & (slots < NB * BS)
+    w.slot_mapping = np.where(good, slots, -1)
+    oc = oracle_write(kind, w, ks, vs)
+    assert_rows_equal(c, oc, np.arange(NB * BS))
