@@ -64,6 +64,16 @@ int main(void) {
          QKV_ERR_BAD_SHAPE);
   expect("topk no rows", qsa_topk_select(NULL, QKV_FP16, 0, 0, NULL, 1, NULL, NULL, 0, NULL),
          QKV_OK);
+  /* the no-alloc decode: the same argument checks, then its scratch limit
+     (40 rows x 16 heads x 64 splits x 256 floats is 40 MiB > 16 MiB) */
+  expect("noalloc splits", qsa_sparse_attn_decode_noalloc(&c, &a, 65, NULL),
+         QKV_ERR_UNSUPPORTED);
+  a.num_rows = 40;
+  a.num_q_heads = 16;
+  expect("noalloc oversize", qsa_sparse_attn_decode_noalloc(&c, &a, 64, NULL), QKV_ERR_SCRATCH);
+  a.num_rows = 0;
+  expect("noalloc no rows", qsa_sparse_attn_decode_noalloc(&c, &a, 8, NULL), QKV_OK);
+  a.num_rows = 1;
   if (qsa_topk_workspace_bytes(40, 131072, 2048) == 0) ++fails;
   if (qsa_decode_workspace_bytes(40, 16, 256, 8) == 0) ++fails;
   if (fails == 0) printf("ok\n");
