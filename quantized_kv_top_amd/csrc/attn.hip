@@ -566,7 +566,7 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
   if (my_n > 0) issue_tile<KIND, D, TT>(ta, p, g, ts(0));
   if (my_n > 1) issue_tile<KIND, D, TT>(tb, p, g, ts(1));
 
-  // ---- Q operand (B of QK^T), the logit factor and the int8 bias term ----
+  // ---- Q operand (B of QK^T) and the logit factor --------------------------
   QOp<KIND> qop[G::kQK];
   float kfac;
   if constexpr (KIND == kBF16) {

@@ -73,7 +73,7 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
 // Two signed int8 codes in bytes (b_lo, b_hi) of `x` -- already XOR-ed with
 // 0x80 so that each byte holds q + 128 -- become the fp16 pair
 // (1152 + q_lo, 1152 + q_hi): 0x64XX is the fp16 value 1024 + XX, exact for
-// XX < 256.  The constant 1152 is removed after the dot product.
+// XX < 256.  The constant 1152 is taken off before the MFMA (i8pair_unbias).
 __device__ __forceinline__ uint32_t i8pair_to_f16x2(uint32_t x_biased, uint32_t sel) {
   return perm(0x64646464u, x_biased, sel);
 }
