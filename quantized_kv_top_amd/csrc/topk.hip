@@ -457,13 +457,21 @@ __device__ __forceinline__ void select_row(Smem& s, uint32_t* s_cand, const RegK
   }
 
   // ---- the list ---------------------------------------------------------------
+  // four consecutive candidates per thread: one block scan covers the whole
+  // candidate buffer (position order is thread order, then element order)
   const uint32_t T = st.pval, ties = st.need, n_gt = (uint32_t)k - ties;
   uint32_t gt_base = 0, eq_base = 0;
-  for (int c0 = 0; c0 < (int)ncand; c0 += kThreads) {
-    const int i = c0 + tid;
-    const uint32_t kk[1] = {i < (int)ncand ? s_key[i] : 0u};
-    const int ix[1] = {i < (int)ncand ? s_idx[i] : -1};
-    emit_tile<1>(bs, row, o, kk, ix, T, ties, gt_base, eq_base);
+  constexpr int kPerThread = 4;
+  for (int c0 = 0; c0 < (int)ncand; c0 += kPerThread * kThreads) {
+    uint32_t kk[kPerThread];
+    int ix[kPerThread];
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      const int i = c0 + kPerThread * tid + e;
+      kk[e] = i < (int)ncand ? s_key[i] : 0u;
+      ix[e] = i < (int)ncand ? s_idx[i] : -1;
+    }
+    emit_tile<kPerThread>(bs, row, o, kk, ix, T, ties, gt_base, eq_base);
     if (gt_base == n_gt && eq_base >= ties) break;       // uniform
   }
 }
